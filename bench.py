@@ -1,0 +1,181 @@
+"""Benchmark of the chunked Mamba-2 SSD forward pass on one MI355X.
+
+One step = one mamba2_ssd_forward (chunk_cumsum -> chunk_state ->
+state_passing -> chunk_scan) over the whole workload, inputs resident in HBM.
+Prints one JSON line with tokens/s, the roofline position of the dominant
+kernel (per-kernel durations measured here with HIP events on the launch
+stream) and the CPU oracle's throughput on the host as a reported baseline.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload long_L64k_N256]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD forward tokens/s at L=64K,N=256 on 1 MI355X; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, TFLOP/s
+RIDGE = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+STAGES = ("chunk_cumsum", "chunk_state", "state_passing", "chunk_scan")
+
+
+def stage_model(w):
+    """Algorithmic flops and HBM bytes per launch of each stage: every input
+    read once and every output written once; flops count the causal triangle
+    (diagonal included) and nothing above it."""
+    B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
+    nc = w.nchunks
+    e = 4 if w.dtype == "f32" else 2
+    tok, csb = B * L, B * H * nc * Q * 4
+    st = B * nc * H * P * N * 4
+    x = tok * H * P * e
+    bc = tok * G * N * e
+    m = {}
+    m["chunk_cumsum"] = dict(flops=2 * tok * H, bytes=tok * H * e + H * 4 + 2 * csb)
+    m["chunk_state"] = dict(flops=2 * N * P * tok * H, bytes=x + bc + 2 * csb + st)
+    m["state_passing"] = dict(flops=2 * st // 4, bytes=2 * st + B * H * nc * 4)
+    m["chunk_scan"] = dict(
+        flops=tok * H * (2 * N * P + (Q + 1) * N + (Q + 1) * P + 2 * P),
+        bytes=x + 2 * bc + 2 * csb + st + H * 4 + x)
+    return m
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_L64k_N256")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens per head for the CPU oracle sample (0 = whole sequence)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import ssd_inputs
+    import state_space_sequence_02_amd as m2
+
+    w = ssd_inputs.WORKLOADS[args.workload]
+    inp = ssd_inputs.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    dims = m2.dims_of(g["x"], g["B"], w.chunk_size)
+    y = torch.empty_like(g["x"])
+    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    need = m2.mamba2_ssd_workspace_bytes(dims)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        m2.mamba2_ssd_forward(dims, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"],
+                              g["init_state"], y, fin, ws, need, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # Per-stage durations: the same four launches through the stage entry points,
+    # bracketed by events on the launch stream.
+    cs, dtt, st = m2.stage_buffers(dims, dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for it in range(args.steps + 1):
+        e = evs[it - 1] if it > 0 else None
+        if e: e[0].record(stream)
+        m2.mamba2_chunk_cumsum(dims, g["dt"], g["A"], cs, dtt, stream)
+        if e: e[1].record(stream)
+        m2.mamba2_chunk_state(dims, g["x"], g["B"], cs, dtt, st, stream)
+        if e: e[2].record(stream)
+        m2.mamba2_state_passing(dims, st, cs, g["init_state"], fin, stream)
+        if e: e[3].record(stream)
+        m2.mamba2_chunk_scan(dims, g["x"], g["B"], g["C"], cs, dtt, st, g["D"], y, stream)
+        if e: e[4].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = {s: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+                for i, s in enumerate(STAGES)}
+    model = stage_model(w)
+    dom = max(STAGES, key=lambda s: stage_ms[s])
+    dm = model[dom]
+    ai = dm["flops"] / dm["bytes"]
+    bound = "hbm" if ai < RIDGE else "mfma"
+    if bound == "hbm":
+        achieved = dm["bytes"] / (stage_ms[dom] * 1e-3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = dm["flops"] / (stage_ms[dom] * 1e-3) / 1e12
+        peak, unit = BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
+    stages = {}
+    for s in STAGES:
+        t = stage_ms[s] * 1e-3
+        stages[s] = {"ms": round(stage_ms[s], 4),
+                     "GB/s": round(model[s]["bytes"] / t / 1e9, 1),
+                     "TFLOP/s": round(model[s]["flops"] / t / 1e12, 2),
+                     "hbm_frac": round(model[s]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 3)}
+
+    tokens = w.tokens
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "wall_ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk_size": w.chunk_size, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak, "traffic": None,
+                     "algorithmic_bytes": dm["bytes"], "algorithmic_flops": dm["flops"]},
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(inp, w, tokens_per_head):
+    """The CPU oracle (direct float64 recurrence, OpenMP) on the host, on a
+    bounded prefix of the same inputs; tokens/s over all heads."""
+    import oracle
+    Ls = w.seqlen if tokens_per_head <= 0 else min(w.seqlen, tokens_per_head)
+    o = {k: (None if v is None else v[:, :Ls].float().numpy() if k in ("x", "dt", "B", "C")
+             else v.float().numpy()) for k, v in inp.items()}
+    t0 = time.perf_counter()
+    oracle.ssd_recurrence(o["x"], o["dt"], o["A"], o["B"], o["C"], o["D"], o["init_state"],
+                          chunk_size=w.chunk_size, want_final=True)
+    dt = time.perf_counter() - t0
+    return {"value": w.batch * Ls / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"first {Ls} of {w.seqlen} tokens, all {w.nheads} heads, batch {w.batch}"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * mamba2_ssd.h - C ABI of the MI355X (gfx950) chunked Mamba-2 SSD forward pass.
+ *
+ * The method (pages: devotd.net news item on the Mamba-2 CUDA Tile
+ * forward-pass kernels, sections 1-2; disconfirmai.com "Jane Street ML
+ * Engineers Map Mamba-2 Recurrent State Computation to Tensor Cores with
+ * cuTile", abstract and body) evaluates the recurrence
+ *
+ *     h_t = exp(dt_t * A) * h_{t-1} + dt_t * x_t (outer) B_t      state [P, N]
+ *     y_t = h_t . C_t + D * x_t
+ *
+ * chunk by chunk: an in-chunk log-space cumulative sum of dt*A
+ * (chunk_cumsum), per-chunk B X^T contractions and the decayed jump that
+ * carries the state across chunks in order (fwd_pass_state, exposed here as
+ * chunk_state + state_passing), and the fused output stage (compute_out,
+ * exposed as chunk_scan): carried-state term C.h, the causally masked,
+ * decay-weighted C B^T interaction times X, and the D skip.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Sizes: B = batch, L = seqlen, H = nheads, P = headdim, N = dstate,
+ *        G = ngroups (H % G == 0; head h reads B/C group h / (H/G)),
+ *        Q = chunk_size, nc = ceil(L / Q).
+ * Layouts (contiguous, row-major, innermost last):
+ *        x, y          [B, L, H, P]
+ *        dt            [B, L, H]
+ *        A, D          [H]                 float32
+ *        B, C          [B, L, G, N]
+ *        init/final    [B, H, P, N]        float32
+ *        dA_cs, dt_T   [B, H, nc, Q]       float32 (time contiguous)
+ *        states        [B, nc, H, P, N]    float32
+ * dtype: MAMBA2_DTYPE_F32  - every tensor is float32;
+ *        MAMBA2_DTYPE_BF16 - x, dt, B, C and y are bfloat16; A, D, the
+ *                            cumsum outputs, states and the initial/final
+ *                            state are float32.
+ * Positions past L inside the last chunk are treated as zero input (dt = 0,
+ * x = 0), following the zero-padded tile loads of the pages' chunk_cumsum
+ * figure; y is written only for t < L.
+ * Memory: every pointer is device memory owned by the caller.  The library
+ * never allocates or frees and keeps no pointer after a call returns.  Every
+ * pointer must be 16-byte aligned (MAMBA2_ERR_ALIGN otherwise).
+ * Streams: `stream` is a hipStream_t (NULL = default stream).  Every call
+ * only enqueues work on that stream; there is no device synchronisation
+ * inside.  Stages given the same stream run in call order.
+ * Errors: every int-returning call returns a mamba2_status.  Arguments are
+ * checked on the host before anything is enqueued; on a failed check nothing
+ * is launched and no output is touched.  MAMBA2_ERR_HIP reports a launch
+ * failure, with the HIP error text in mamba2_last_error().  No C++ exception
+ * crosses this interface.  Calls are thread-safe: the library keeps no
+ * mutable global state except the calling thread's last-error message.
+ * Preconditions that are not checked (checking would cost a pass over the
+ * data): A <= 0, dt >= 0 and every input finite - the decay regime the
+ * method describes (decay rate times time interval).
+ * Supported sizes: Q in {16, 32, 64, 128, 256} for float32 and
+ * {64, 128, 256} for bfloat16; bfloat16 also needs P in {32, 64, 128} and
+ * N a multiple of 64 with N <= 512.  Other sizes give MAMBA2_ERR_UNSUPPORTED.
+ */
+#ifndef MAMBA2_SSD_H_
+#define MAMBA2_SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MAMBA2_OK = 0,
+  MAMBA2_ERR_NULL = 1,        /* a required pointer is NULL */
+  MAMBA2_ERR_SHAPE = 2,       /* non-positive size, H % G != 0, overflow */
+  MAMBA2_ERR_DTYPE = 3,       /* unknown dtype code */
+  MAMBA2_ERR_UNSUPPORTED = 4, /* valid but not implemented size */
+  MAMBA2_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+  MAMBA2_ERR_WORKSPACE = 6,   /* workspace missing or too small */
+  MAMBA2_ERR_HIP = 7          /* a HIP launch failed */
+} mamba2_status;
+
+typedef enum { MAMBA2_DTYPE_F32 = 0, MAMBA2_DTYPE_BF16 = 1 } mamba2_dtype;
+
+typedef struct {
+  int64_t batch;      /* B  >= 1 */
+  int64_t seqlen;     /* L  >= 1 */
+  int64_t nheads;     /* H  >= 1 */
+  int64_t headdim;    /* P  >= 1 */
+  int64_t dstate;     /* N  >= 1 */
+  int64_t ngroups;    /* G  >= 1, divides H */
+  int64_t chunk_size; /* Q */
+  int32_t dtype;      /* mamba2_dtype */
+  int32_t reserved;   /* must be 0 */
+} mamba2_dims;
+
+/* Checks `dims` alone (host only, touches no device).  Returns MAMBA2_OK when
+ * every entry point supports these sizes. */
+int mamba2_validate(const mamba2_dims* dims);
+
+/*
+ * chunk_cumsum (devotd.net page, section 2 and its code figure): for every
+ * batch b, head h and chunk c, the inclusive cumulative sum of A[h]*dt along
+ * the chunk's time steps, multiplied by log2(e) so consumers use base-2
+ * exponentials:
+ *     dA_cs[b,h,c,i] = log2(e) * sum_{j<=i} A[h] * dt[b, c*Q+j, h]
+ *     dt_T[b,h,c,i]  = dt[b, c*Q+i, h]        (0 past L)
+ * Inputs dt (dtype of dims), A (float32).  Outputs float32 [B,H,nc,Q],
+ * fully overwritten.  The sum is evaluated as a tree (wavefront scan).
+ */
+int mamba2_chunk_cumsum(const mamba2_dims* dims, const void* dt, const float* A,
+                        float* dA_cs, float* dt_T, void* stream);
+
+/*
+ * chunk_state (first half of fwd_pass_state; disconfirmai.com page, body:
+ * the jump formula's B X^T product with rows pre-scaled by exponentials): the
+ * state each chunk reaches from a zero start,
+ *     states[b,c,h,p,n] = sum_{j in chunk} 2^(cs[Q-1] - cs[j]) * dt_j
+ *                                          * x[b,cQ+j,h,p] * B[b,cQ+j,g,n]
+ * with cs = dA_cs[b,h,c,:], dt_j = dt_T[b,h,c,j].  Inputs x, B (dtype of
+ * dims), dA_cs and dt_T from mamba2_chunk_cumsum.  Output states float32
+ * [B,nc,H,P,N], fully overwritten.
+ */
+int mamba2_chunk_state(const mamba2_dims* dims, const void* x, const void* B,
+                       const float* dA_cs, const float* dt_T, float* states,
+                       void* stream);
+
+/*
+ * state_passing (second half of fwd_pass_state; devotd.net page, section 2:
+ * the state at each chunk start and after the last chunk, chunks in order,
+ * independent parts of the state in parallel).  In place over `states`:
+ *     run = init_state (zeros if NULL)
+ *     for c in 0..nc-1:  S = states[b,c,h];  states[b,c,h] = run;
+ *                        run = 2^(dA_cs[b,h,c,Q-1]) * run + S
+ *     final_state = run                   (not written if NULL)
+ * On entry states holds chunk_state's per-chunk states; on return it holds
+ * the state at the start of every chunk.  All float32.
+ */
+int mamba2_state_passing(const mamba2_dims* dims, float* states, const float* dA_cs,
+                         const float* init_state, float* final_state, void* stream);
+
+/*
+ * chunk_scan = compute_out (devotd.net page, section 2; disconfirmai.com
+ * page, abstract): outputs of every chunk from its start state, fused so the
+ * Q x Q interaction matrix never reaches memory.  For token i of chunk c,
+ * head h, group g:
+ *     y[i,p] = 2^cs[i] * sum_n C[i,n] h[p,n]
+ *            + sum_{j<=i} (sum_n C[i,n] B[j,n]) 2^(cs[i]-cs[j]) dt_j x[j,p]
+ *            + D[h] x[i,p]
+ * with h = states[b,c,h] (chunk-start states from mamba2_state_passing),
+ * cs = dA_cs[b,h,c,:], dt = dt_T[b,h,c,:].  D may be NULL (no skip term).
+ * Output y (dtype of dims) [B,L,H,P]; rows t >= L are not written.
+ */
+int mamba2_chunk_scan(const mamba2_dims* dims, const void* x, const void* B,
+                      const void* C, const float* dA_cs, const float* dt_T,
+                      const float* states, const float* D, void* y, void* stream);
+
+/* Bytes of device workspace mamba2_ssd_forward needs for `dims` (0 if the
+ * dims are invalid).  Host only. */
+size_t mamba2_ssd_workspace_bytes(const mamba2_dims* dims);
+
+/*
+ * The whole forward pass: chunk_cumsum -> chunk_state -> state_passing ->
+ * chunk_scan on `stream`, intermediates in the caller's workspace (at least
+ * mamba2_ssd_workspace_bytes(dims) bytes, 256-byte aligned; contents on
+ * return are unspecified).  init_state and D may be NULL; final_state may
+ * be NULL (not written).  Outputs y [B,L,H,P] (dtype of dims) and
+ * final_state [B,H,P,N] float32.
+ */
+int mamba2_ssd_forward(const mamba2_dims* dims, const void* x, const void* dt,
+                       const float* A, const void* B, const void* C, const float* D,
+                       const float* init_state, void* y, float* final_state,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* mamba2_status_string(int status);
+
+/* Detail of the calling thread's most recent failure ("" if none). */
+const char* mamba2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA2_SSD_H_ */

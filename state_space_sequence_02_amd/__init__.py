@@ -1,0 +1,201 @@
+"""Python binding of the MI355X (gfx950) Mamba-2 SSD forward-pass library.
+
+Thin ctypes marshalling over ``libmamba2_ssd.so`` (C ABI in
+``include/mamba2_ssd.h``): every step of the forward pass runs in the HIP
+kernels; this module only turns torch tensors into device pointers and the
+current torch stream into a ``hipStream_t``.  The functions keep the C names:
+
+    mamba2_validate, mamba2_chunk_cumsum, mamba2_chunk_state,
+    mamba2_state_passing, mamba2_chunk_scan, mamba2_ssd_workspace_bytes,
+    mamba2_ssd_forward, mamba2_status_string, mamba2_last_error
+
+plus ``make_dims`` and ``ssd_forward`` (allocates outputs and workspace with
+torch, then calls ``mamba2_ssd_forward``).  Importing fails loudly when the
+library has not been built; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmamba2_ssd.so")
+
+MAMBA2_OK = 0
+MAMBA2_ERR_NULL = 1
+MAMBA2_ERR_SHAPE = 2
+MAMBA2_ERR_DTYPE = 3
+MAMBA2_ERR_UNSUPPORTED = 4
+MAMBA2_ERR_ALIGN = 5
+MAMBA2_ERR_WORKSPACE = 6
+MAMBA2_ERR_HIP = 7
+
+MAMBA2_DTYPE_F32 = 0
+MAMBA2_DTYPE_BF16 = 1
+
+EXPORTS = (
+    "mamba2_validate", "mamba2_chunk_cumsum", "mamba2_chunk_state", "mamba2_state_passing",
+    "mamba2_chunk_scan", "mamba2_ssd_workspace_bytes", "mamba2_ssd_forward",
+    "mamba2_status_string", "mamba2_last_error",
+)
+
+
+class Mamba2Dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+        ("chunk_size", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+    def __repr__(self):
+        return "Mamba2Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class Mamba2Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {mamba2_status_string(status)} ({mamba2_last_error()})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python __graft_entry__.py build` "
+            "(or state_space_sequence_02_amd/build.py); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(Mamba2Dims)
+    sig = {
+        "mamba2_validate": ([D], ctypes.c_int),
+        "mamba2_chunk_cumsum": ([D, P, P, P, P, P], ctypes.c_int),
+        "mamba2_chunk_state": ([D, P, P, P, P, P, P], ctypes.c_int),
+        "mamba2_state_passing": ([D, P, P, P, P, P], ctypes.c_int),
+        "mamba2_chunk_scan": ([D, P, P, P, P, P, P, P, P, P], ctypes.c_int),
+        "mamba2_ssd_workspace_bytes": ([D], ctypes.c_size_t),
+        "mamba2_ssd_forward": ([D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P], ctypes.c_int),
+        "mamba2_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "mamba2_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != MAMBA2_OK:
+        raise Mamba2Error(status, where)
+
+
+def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype) -> Mamba2Dims:
+    """dtype: torch.float32 / torch.bfloat16 or the MAMBA2_DTYPE_* code."""
+    if dtype is torch.float32:
+        dtype = MAMBA2_DTYPE_F32
+    elif dtype is torch.bfloat16:
+        dtype = MAMBA2_DTYPE_BF16
+    return Mamba2Dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, int(dtype), 0)
+
+
+def dims_of(x: torch.Tensor, B: torch.Tensor, chunk_size: int) -> Mamba2Dims:
+    """Dims from x[B,L,H,P] and B[B,L,G,N]."""
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return make_dims(b, L, H, P, N, G, chunk_size, x.dtype)
+
+
+def mamba2_validate(dims) -> int:
+    return int(_lib.mamba2_validate(ctypes.byref(dims)))
+
+
+def mamba2_status_string(status: int) -> str:
+    return _lib.mamba2_status_string(int(status)).decode()
+
+
+def mamba2_last_error() -> str:
+    return _lib.mamba2_last_error().decode()
+
+
+def mamba2_ssd_workspace_bytes(dims) -> int:
+    return int(_lib.mamba2_ssd_workspace_bytes(ctypes.byref(dims)))
+
+
+def mamba2_chunk_cumsum(dims, dt, A, dA_cs, dt_T, stream=None):
+    _check(_lib.mamba2_chunk_cumsum(ctypes.byref(dims), _ptr(dt), _ptr(A), _ptr(dA_cs),
+                                    _ptr(dt_T), _stream(stream)), "mamba2_chunk_cumsum")
+
+
+def mamba2_chunk_state(dims, x, B, dA_cs, dt_T, states, stream=None):
+    _check(_lib.mamba2_chunk_state(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(dA_cs), _ptr(dt_T),
+                                   _ptr(states), _stream(stream)), "mamba2_chunk_state")
+
+
+def mamba2_state_passing(dims, states, dA_cs, init_state, final_state, stream=None):
+    _check(_lib.mamba2_state_passing(ctypes.byref(dims), _ptr(states), _ptr(dA_cs),
+                                     _ptr(init_state), _ptr(final_state), _stream(stream)),
+           "mamba2_state_passing")
+
+
+def mamba2_chunk_scan(dims, x, B, C, dA_cs, dt_T, states, D, y, stream=None):
+    _check(_lib.mamba2_chunk_scan(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(C), _ptr(dA_cs),
+                                  _ptr(dt_T), _ptr(states), _ptr(D), _ptr(y), _stream(stream)),
+           "mamba2_chunk_scan")
+
+
+def mamba2_ssd_forward(dims, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                       workspace_bytes, stream=None):
+    _check(_lib.mamba2_ssd_forward(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                   _ptr(C), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
+                                   _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "mamba2_ssd_forward")
+
+
+def ssd_forward(x, dt, A, B, C, D=None, init_state=None, *, chunk_size=256, workspace=None,
+                stream=None):
+    """Allocates y, the final state and (unless given) the workspace with torch on x's
+    device, runs mamba2_ssd_forward, and returns (y, final_state)."""
+    dims = dims_of(x, B, chunk_size)
+    y = torch.empty_like(x)
+    final = torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]), dtype=torch.float32,
+                        device=x.device)
+    need = mamba2_ssd_workspace_bytes(dims)
+    if need == 0:
+        _check(mamba2_validate(dims), "ssd_forward")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    mamba2_ssd_forward(dims, x, dt, A, B, C, D, init_state, y, final, workspace,
+                       workspace.numel() * workspace.element_size(), stream)
+    return y, final
+
+
+def stage_buffers(dims, device):
+    """Allocates the per-stage intermediates: dA_cs, dt_T [B,H,nc,Q] and states
+    [B,nc,H,P,N], all float32."""
+    nc = -(-dims.seqlen // dims.chunk_size)
+    cs = torch.empty((dims.batch, dims.nheads, nc, dims.chunk_size), dtype=torch.float32,
+                     device=device)
+    dtt = torch.empty_like(cs)
+    st = torch.empty((dims.batch, nc, dims.nheads, dims.headdim, dims.dstate),
+                     dtype=torch.float32, device=device)
+    return cs, dtt, st

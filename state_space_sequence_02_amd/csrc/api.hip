@@ -1,0 +1,255 @@
+// C ABI of the SSD forward pass: argument checks on the host, workspace
+// carving, and stream-ordered launches of the stage kernels.  Declarations and
+// the contract of every entry point are in include/mamba2_ssd.h.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "launch.h"
+#include "mamba2_ssd.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return MAMBA2_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Upper bounds that keep every index and grid size inside the kernels' types.
+constexpr int64_t kMaxSeq = (int64_t)1 << 30;
+constexpr int64_t kMaxUnits = (int64_t)1 << 26;   // B * nc * H workgroups
+constexpr int64_t kMaxElems = (int64_t)1 << 40;   // elements of any tensor
+
+int validate(const mamba2_dims* d, m2::Dims* out) {
+  if (!d) return fail(MAMBA2_ERR_NULL, "dims is NULL");
+  if (d->dtype != MAMBA2_DTYPE_F32 && d->dtype != MAMBA2_DTYPE_BF16)
+    return fail(MAMBA2_ERR_DTYPE, "unknown dtype code %d", (int)d->dtype);
+  if (d->reserved != 0) return fail(MAMBA2_ERR_SHAPE, "dims.reserved must be 0");
+  if (d->batch < 1 || d->seqlen < 1 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+      d->ngroups < 1 || d->chunk_size < 1)
+    return fail(MAMBA2_ERR_SHAPE,
+                "sizes must be >= 1 (batch=%lld seqlen=%lld nheads=%lld headdim=%lld "
+                "dstate=%lld ngroups=%lld chunk_size=%lld)",
+                (long long)d->batch, (long long)d->seqlen, (long long)d->nheads,
+                (long long)d->headdim, (long long)d->dstate, (long long)d->ngroups,
+                (long long)d->chunk_size);
+  if (d->nheads % d->ngroups != 0)
+    return fail(MAMBA2_ERR_SHAPE, "nheads (%lld) is not a multiple of ngroups (%lld)",
+                (long long)d->nheads, (long long)d->ngroups);
+  const int64_t Q = d->chunk_size;
+  const bool bf = d->dtype == MAMBA2_DTYPE_BF16;
+  if (bf) {
+    if (Q != 64 && Q != 128 && Q != 256)
+      return fail(MAMBA2_ERR_UNSUPPORTED, "bfloat16 chunk_size must be 64, 128 or 256 (got %lld)",
+                  (long long)Q);
+    if (d->headdim != 32 && d->headdim != 64 && d->headdim != 128)
+      return fail(MAMBA2_ERR_UNSUPPORTED, "bfloat16 headdim must be 32, 64 or 128 (got %lld)",
+                  (long long)d->headdim);
+    if (d->dstate % 64 != 0 || d->dstate > 512)
+      return fail(MAMBA2_ERR_UNSUPPORTED,
+                  "bfloat16 dstate must be a multiple of 64 and at most 512 (got %lld)",
+                  (long long)d->dstate);
+  } else {
+    if (Q != 16 && Q != 32 && Q != 64 && Q != 128 && Q != 256)
+      return fail(MAMBA2_ERR_UNSUPPORTED,
+                  "float32 chunk_size must be 16, 32, 64, 128 or 256 (got %lld)", (long long)Q);
+    if (d->headdim > 1024 || d->dstate > 4096)
+      return fail(MAMBA2_ERR_UNSUPPORTED, "float32 headdim <= 1024 and dstate <= 4096 required");
+  }
+  if (d->seqlen > kMaxSeq || d->nheads > 65536 || d->batch > 65536)
+    return fail(MAMBA2_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  const int64_t nc = (d->seqlen + Q - 1) / Q;
+  const double units = (double)d->batch * (double)nc * (double)d->nheads;
+  const double st = units * (double)d->headdim * (double)d->dstate;
+  const double xs = (double)d->batch * (double)d->seqlen * (double)d->nheads * (double)d->headdim;
+  if (units > (double)kMaxUnits || st > (double)kMaxElems || xs > (double)kMaxElems)
+    return fail(MAMBA2_ERR_UNSUPPORTED, "problem too large for one call");
+  if (out) {
+    out->B = d->batch;
+    out->L = d->seqlen;
+    out->H = d->nheads;
+    out->P = d->headdim;
+    out->N = d->dstate;
+    out->G = d->ngroups;
+    out->Q = Q;
+    out->nc = nc;
+    out->bf16 = bf;
+  }
+  return MAMBA2_OK;
+}
+
+int need(const void* p, const char* name) {
+  if (!p) return fail(MAMBA2_ERR_NULL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MAMBA2_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return MAMBA2_OK;
+}
+
+int maybe(const void* p, const char* name) {
+  if (p && !aligned16(p)) return fail(MAMBA2_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return MAMBA2_OK;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(MAMBA2_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Workspace {
+  size_t cs_bytes, st_bytes, total;
+};
+
+Workspace plan(const m2::Dims& d) {
+  Workspace w;
+  w.cs_bytes = round256((size_t)(d.B * d.H * d.nc * d.Q) * sizeof(float));
+  w.st_bytes = round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * sizeof(float));
+  w.total = 2 * w.cs_bytes + w.st_bytes;
+  return w;
+}
+
+#define CHECK(expr)               \
+  do {                            \
+    const int rc_ = (expr);       \
+    if (rc_ != MAMBA2_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int mamba2_validate(const mamba2_dims* dims) {
+  CHECK(validate(dims, nullptr));
+  return ok();
+}
+
+int mamba2_chunk_cumsum(const mamba2_dims* dims, const void* dt, const float* A, float* dA_cs,
+                        float* dt_T, void* stream) {
+  m2::Dims d;
+  CHECK(validate(dims, &d));
+  CHECK(need(dt, "dt"));
+  CHECK(need(A, "A"));
+  CHECK(need(dA_cs, "dA_cs"));
+  CHECK(need(dt_T, "dt_T"));
+  return hip_status(m2::launch_chunk_cumsum(d, dt, A, dA_cs, dt_T, (hipStream_t)stream),
+                    "chunk_cumsum launch");
+}
+
+int mamba2_chunk_state(const mamba2_dims* dims, const void* x, const void* B, const float* dA_cs,
+                       const float* dt_T, float* states, void* stream) {
+  m2::Dims d;
+  CHECK(validate(dims, &d));
+  CHECK(need(x, "x"));
+  CHECK(need(B, "B"));
+  CHECK(need(dA_cs, "dA_cs"));
+  CHECK(need(dt_T, "dt_T"));
+  CHECK(need(states, "states"));
+  return hip_status(m2::launch_chunk_state(d, x, B, dA_cs, dt_T, states, (hipStream_t)stream),
+                    "chunk_state launch");
+}
+
+int mamba2_state_passing(const mamba2_dims* dims, float* states, const float* dA_cs,
+                         const float* init_state, float* final_state, void* stream) {
+  m2::Dims d;
+  CHECK(validate(dims, &d));
+  CHECK(need(states, "states"));
+  CHECK(need(dA_cs, "dA_cs"));
+  CHECK(maybe(init_state, "init_state"));
+  CHECK(maybe(final_state, "final_state"));
+  return hip_status(
+      m2::launch_state_passing(d, states, dA_cs, init_state, final_state, (hipStream_t)stream),
+      "state_passing launch");
+}
+
+int mamba2_chunk_scan(const mamba2_dims* dims, const void* x, const void* B, const void* C,
+                      const float* dA_cs, const float* dt_T, const float* states, const float* D,
+                      void* y, void* stream) {
+  m2::Dims d;
+  CHECK(validate(dims, &d));
+  CHECK(need(x, "x"));
+  CHECK(need(B, "B"));
+  CHECK(need(C, "C"));
+  CHECK(need(dA_cs, "dA_cs"));
+  CHECK(need(dt_T, "dt_T"));
+  CHECK(need(states, "states"));
+  CHECK(maybe(D, "D"));
+  CHECK(need(y, "y"));
+  return hip_status(
+      m2::launch_chunk_scan(d, x, B, C, dA_cs, dt_T, states, D, y, (hipStream_t)stream),
+      "chunk_scan launch");
+}
+
+size_t mamba2_ssd_workspace_bytes(const mamba2_dims* dims) {
+  m2::Dims d;
+  if (validate(dims, &d) != MAMBA2_OK) return 0;
+  return plan(d).total;
+}
+
+int mamba2_ssd_forward(const mamba2_dims* dims, const void* x, const void* dt, const float* A,
+                       const void* B, const void* C, const float* D, const float* init_state,
+                       void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  m2::Dims d;
+  CHECK(validate(dims, &d));
+  CHECK(need(x, "x"));
+  CHECK(need(dt, "dt"));
+  CHECK(need(A, "A"));
+  CHECK(need(B, "B"));
+  CHECK(need(C, "C"));
+  CHECK(maybe(D, "D"));
+  CHECK(maybe(init_state, "init_state"));
+  CHECK(need(y, "y"));
+  CHECK(maybe(final_state, "final_state"));
+  const Workspace w = plan(d);
+  if (!workspace) return fail(MAMBA2_ERR_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(MAMBA2_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < w.total)
+    return fail(MAMBA2_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                w.total);
+  char* ws = (char*)workspace;
+  float* dA_cs = (float*)ws;
+  float* dt_T = (float*)(ws + w.cs_bytes);
+  float* states = (float*)(ws + 2 * w.cs_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = m2::launch_chunk_cumsum(d, dt, A, dA_cs, dt_T, s);
+  if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
+  e = m2::launch_chunk_state(d, x, B, dA_cs, dt_T, states, s);
+  if (e != hipSuccess) return hip_status(e, "chunk_state launch");
+  e = m2::launch_state_passing(d, states, dA_cs, init_state, final_state, s);
+  if (e != hipSuccess) return hip_status(e, "state_passing launch");
+  e = m2::launch_chunk_scan(d, x, B, C, dA_cs, dt_T, states, D, y, s);
+  return hip_status(e, "chunk_scan launch");
+}
+
+const char* mamba2_status_string(int status) {
+  switch (status) {
+    case MAMBA2_OK: return "ok";
+    case MAMBA2_ERR_NULL: return "a required pointer is NULL";
+    case MAMBA2_ERR_SHAPE: return "invalid sizes";
+    case MAMBA2_ERR_DTYPE: return "unknown dtype";
+    case MAMBA2_ERR_UNSUPPORTED: return "sizes not supported by this library";
+    case MAMBA2_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MAMBA2_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MAMBA2_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* mamba2_last_error(void) { return g_last_error; }
+
+}  // extern "C"

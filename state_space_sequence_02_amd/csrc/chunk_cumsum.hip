@@ -1,0 +1,106 @@
+// chunk_cumsum: in-chunk cumulative sum of the log-decay A*dt, in log2 units
+// (devotd.net news item on the Mamba-2 CUDA Tile forward-pass kernels,
+// section 2 and its chunk_cumsum code figure: zero-padded dt tile, float cast,
+// inclusive cumsum along the chunk, times LOG2E; section 3: the cumsum and dt
+// stored so later stages read them contiguously).
+//
+// One workgroup per (chunk, head tile, batch); thread i owns time step i of
+// the chunk.  The sum is a tree: a Kogge-Stone scan inside each 64-lane
+// wavefront, then the wave totals added through LDS.  Every partial sum is of
+// same-sign terms (A <= 0, dt >= 0), so its relative error grows with the
+// tree depth (at most 9 roundings for Q = 256) rather than with Q.
+//
+// Outputs are time-contiguous [B, H, nc, Q] float32: dA_cs (log2 units) and
+// dt_T (dt transposed, 0 past the end of the sequence).
+#include "common.h"
+#include "launch.h"
+
+namespace m2 {
+
+namespace {
+
+constexpr int kHeadTile = 16;
+
+template <typename T>
+__device__ __forceinline__ float load_f32(const T* p);
+template <>
+__device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load_f32<bf16>(const bf16* p) { return bf2f(*p); }
+
+template <typename T>
+__global__ void __launch_bounds__(256) chunk_cumsum_kernel(const T* __restrict__ dt,
+                                                           const float* __restrict__ A,
+                                                           float* __restrict__ dA_cs,
+                                                           float* __restrict__ dt_T, int L, int H,
+                                                           int Q, int nc) {
+  __shared__ float wave_tot[kHeadTile][4];
+  const int c = blockIdx.x;
+  const int h0 = blockIdx.y * kHeadTile;
+  const int b = blockIdx.z;
+  const int i = threadIdx.x;  // time step in the chunk
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int nwaves = (blockDim.x + 63) >> 6;
+  const int t = c * Q + i;
+  const int nh = min(kHeadTile, H - h0);
+
+  float v[kHeadTile];
+  float dtv[kHeadTile];
+#pragma unroll
+  for (int k = 0; k < kHeadTile; ++k) {
+    dtv[k] = 0.f;
+    if (k < nh && i < Q && t < L) dtv[k] = load_f32(dt + ((int64_t)b * L + t) * H + h0 + k);
+    v[k] = (k < nh) ? A[h0 + k] * dtv[k] : 0.f;
+  }
+  // Kogge-Stone inclusive scan within the wavefront.
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < kHeadTile; ++k) {
+      float u = __shfl_up(v[k], off, 64);
+      if (lane >= off) v[k] += u;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < kHeadTile; ++k) wave_tot[k][w] = v[k];
+  }
+  __syncthreads();
+  if (w > 0) {
+#pragma unroll
+    for (int k = 0; k < kHeadTile; ++k) {
+      float pre = wave_tot[k][0];
+      for (int u = 1; u < w; ++u) pre += wave_tot[k][u];
+      v[k] += pre;
+    }
+  }
+  (void)nwaves;
+  if (i < Q) {
+#pragma unroll
+    for (int k = 0; k < kHeadTile; ++k) {
+      if (k < nh) {
+        const int64_t o = (((int64_t)b * H + h0 + k) * nc + c) * Q + i;
+        dA_cs[o] = v[k] * kLog2e;
+        dt_T[o] = dtv[k];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_cumsum(const Dims& d, const void* dt, const float* A, float* dA_cs,
+                               float* dt_T, hipStream_t s) {
+  const int threads = (int)((d.Q + 63) / 64 * 64);
+  dim3 grid((unsigned)d.nc, (unsigned)((d.H + kHeadTile - 1) / kHeadTile), (unsigned)d.B);
+  if (d.bf16)
+    chunk_cumsum_kernel<bf16><<<grid, threads, 0, s>>>((const bf16*)dt, A, dA_cs, dt_T, (int)d.L,
+                                                       (int)d.H, (int)d.Q, (int)d.nc);
+  else
+    chunk_cumsum_kernel<float><<<grid, threads, 0, s>>>((const float*)dt, A, dA_cs, dt_T,
+                                                        (int)d.L, (int)d.H, (int)d.Q, (int)d.nc);
+  return hipGetLastError();
+}
+
+}  // namespace m2

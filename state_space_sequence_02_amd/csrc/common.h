@@ -1,0 +1,56 @@
+// Shared device-side helpers of the gfx950 SSD kernels: vector types, bf16
+// conversions, MFMA wrappers and the LDS transpose read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m2 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// log2(e) rounded to float32: the cumulative sums are stored in log2 units so
+// that every consumer evaluates its decays with the hardware's native 2^x.
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
+// float -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }
+
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16).
+// Operand layout (checked on gfx950): lane l holds A row (l & 15) and B
+// column (l & 15), with K elements 8*(l >> 4) .. 8*(l >> 4) + 7 in vector
+// order; the accumulator lane l holds column (l & 15), rows 4*(l >> 4) + r.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// gfx950 LDS transpose read.  Within each 16-lane group, lane L supplies the
+// address of 4 consecutive 16-bit elements; lane i receives element e from
+// the chunk of lane 4*e + i/4, position i%4.  If lane L points at
+// M[k0 + L/4][c(L%4) .. c(L%4)+3] of a row-major matrix M, lane i = 4q + s
+// receives M[k0 + e][c(q) + s] for e = 0..3: four consecutive rows of one
+// column, i.e. an MFMA operand whose K runs along M's rows.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace m2

@@ -1,0 +1,25 @@
+// Host-side launchers of the SSD kernels.  Sizes are validated by the C ABI
+// layer before any of these is called; each launcher only enqueues.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m2 {
+
+struct Dims {
+  int64_t B, L, H, P, N, G, Q, nc;
+  bool bf16;
+};
+
+hipError_t launch_chunk_cumsum(const Dims& d, const void* dt, const float* A, float* dA_cs,
+                               float* dt_T, hipStream_t s);
+hipError_t launch_chunk_state(const Dims& d, const void* x, const void* B, const float* dA_cs,
+                              const float* dt_T, float* states, hipStream_t s);
+hipError_t launch_state_passing(const Dims& d, float* states, const float* dA_cs,
+                                const float* init, float* final_state, hipStream_t s);
+hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* B, const void* C,
+                             const float* dA_cs, const float* dt_T, const float* states,
+                             const float* D, void* y, hipStream_t s);
+
+}  // namespace m2

@@ -1,0 +1,79 @@
+// state_passing: the decayed jump that carries the state across chunks in
+// chunk order (devotd.net news item on the Mamba-2 CUDA Tile forward-pass
+// kernels, section 2: fwd_pass_state yields the state at every chunk start
+// and after the last chunk, walking chunks in order while independent parts
+// of the state run in parallel; disconfirmai.com "Jane Street ML Engineers
+// Map Mamba-2 Recurrent State Computation to Tensor Cores with cuTile",
+// body: jump formula with the decay as a log-space sum).
+//
+// Work split: one thread per 4 consecutive (p, n) state entries of one
+// (batch, head); every thread walks all chunks in order.  Memory bound: each
+// chunk's state is read once and overwritten once, in place.  Loads run
+// kDepth chunks ahead of use so that enough bytes are in flight per CU.
+#include "common.h"
+#include "launch.h"
+
+namespace m2 {
+
+namespace {
+
+constexpr int kDepth = 16;
+constexpr int kThreads = 256;
+
+// V is float4 when P*N is a multiple of 4 (every bfloat16 size), else float.
+template <typename V>
+__global__ void __launch_bounds__(kThreads) state_passing_kernel(
+    float* __restrict__ states, const float* __restrict__ dA_cs, const float* __restrict__ init,
+    float* __restrict__ final_state, int64_t H, int64_t PNv, int64_t blocks_per_head, int nc,
+    int Q) {
+  const int64_t bh = (int64_t)blockIdx.x / blocks_per_head;  // b * H + h
+  const int64_t gid = ((int64_t)blockIdx.x % blocks_per_head) * kThreads + threadIdx.x;
+  if (gid >= PNv) return;
+  const int64_t b = bh / H, h = bh % H;
+  const int64_t chunk_stride = H * PNv;  // V units between consecutive chunks
+  V* base = (V*)states + (b * nc * H + h) * PNv + gid;
+  const float* cs_last = dA_cs + bh * (int64_t)nc * Q + (Q - 1);
+
+  V run = V{};
+  if (init) run = ((const V*)init)[bh * PNv + gid];
+
+  V buf[kDepth];
+#pragma unroll
+  for (int k = 0; k < kDepth; ++k)
+    if (k < nc) buf[k] = __builtin_nontemporal_load(base + (int64_t)k * chunk_stride);
+
+  for (int c0 = 0; c0 < nc; c0 += kDepth) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      const int c = c0 + k;
+      if (c < nc) {
+        const V cur = buf[k];
+        if (c + kDepth < nc)
+          buf[k] = __builtin_nontemporal_load(base + (int64_t)(c + kDepth) * chunk_stride);
+        const float decay = exp2f(cs_last[(int64_t)c * Q]);
+        __builtin_nontemporal_store(run, base + (int64_t)c * chunk_stride);
+        run = decay * run + cur;
+      }
+    }
+  }
+  if (final_state) ((V*)final_state)[bh * PNv + gid] = run;
+}
+
+}  // namespace
+
+hipError_t launch_state_passing(const Dims& d, float* states, const float* dA_cs,
+                                const float* init, float* final_state, hipStream_t s) {
+  const int64_t PN = d.P * d.N;
+  if (PN % 4 == 0) {
+    const int64_t PNv = PN / 4, bph = (PNv + kThreads - 1) / kThreads;
+    state_passing_kernel<f32x4><<<(unsigned)(d.B * d.H * bph), kThreads, 0, s>>>(
+        states, dA_cs, init, final_state, d.H, PNv, bph, (int)d.nc, (int)d.Q);
+  } else {
+    const int64_t bph = (PN + kThreads - 1) / kThreads;
+    state_passing_kernel<float><<<(unsigned)(d.B * d.H * bph), kThreads, 0, s>>>(
+        states, dA_cs, init, final_state, d.H, PN, bph, (int)d.nc, (int)d.Q);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace m2
