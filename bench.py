@@ -26,24 +26,34 @@ RIDGE = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 STAGES = ("chunk_cumsum", "chunk_state", "state_passing", "chunk_scan")
 
 
+def grouped_path(w):
+    """The fused forward hands the chunk-start states to the output stage as
+    bfloat16 for these sizes (same rule as the library's dispatch)."""
+    return (w.dtype == "bf16" and w.headdim == 64 and w.dstate in (64, 128, 256)
+            and w.chunk_size in (64, 128, 256))
+
+
 def stage_model(w):
-    """Algorithmic flops and HBM bytes per launch of each stage: every input
-    read once and every output written once; flops count the causal triangle
+    """Algorithmic flops and HBM bytes per launch of each stage of the fused
+    forward: every input read once and every output written once, in the
+    dtypes that stage consumes and produces; flops count the causal triangle
     (diagonal included) and nothing above it."""
     B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
     nc = w.nchunks
     e = 4 if w.dtype == "f32" else 2
     tok, csb = B * L, B * H * nc * Q * 4
-    st = B * nc * H * P * N * 4
+    st = B * nc * H * P * N * 4                      # per-chunk states, float32
+    hs = st // 2 if grouped_path(w) else st          # chunk-start states as handed on
+    fin = B * H * P * N * 4
     x = tok * H * P * e
     bc = tok * G * N * e
     m = {}
     m["chunk_cumsum"] = dict(flops=2 * tok * H, bytes=tok * H * e + H * 4 + 2 * csb)
     m["chunk_state"] = dict(flops=2 * N * P * tok * H, bytes=x + bc + 2 * csb + st)
-    m["state_passing"] = dict(flops=2 * st // 4, bytes=2 * st + B * H * nc * 4)
+    m["state_passing"] = dict(flops=2 * st // 4, bytes=st + hs + B * H * nc * 4 + fin)
     m["chunk_scan"] = dict(
         flops=tok * H * (2 * N * P + (Q + 1) * N + (Q + 1) * P + 2 * P),
-        bytes=x + 2 * bc + 2 * csb + st + H * 4 + x)
+        bytes=x + 2 * bc + 2 * csb + hs + H * 4 + x)
     return m
 
 
@@ -56,7 +66,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens per head for the CPU oracle sample (0 = whole sequence)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}))
@@ -96,24 +111,14 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     ms = ev0.elapsed_time(ev1) / args.steps
 
-    # Per-stage durations: the same four launches through the stage entry points,
-    # bracketed by events on the launch stream.
-    cs, dtt, st = m2.stage_buffers(dims, dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for it in range(args.steps + 1):
-        e = evs[it - 1] if it > 0 else None
-        if e: e[0].record(stream)
-        m2.mamba2_chunk_cumsum(dims, g["dt"], g["A"], cs, dtt, stream)
-        if e: e[1].record(stream)
-        m2.mamba2_chunk_state(dims, g["x"], g["B"], cs, dtt, st, stream)
-        if e: e[2].record(stream)
-        m2.mamba2_state_passing(dims, st, cs, g["init_state"], fin, stream)
-        if e: e[3].record(stream)
-        m2.mamba2_chunk_scan(dims, g["x"], g["B"], g["C"], cs, dtt, st, g["D"], y, stream)
-        if e: e[4].record(stream)
-    torch.cuda.synchronize()
-    stage_ms = {s: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-                for i, s in enumerate(STAGES)}
+    # Per-stage durations of the same forward: HIP events recorded on the launch
+    # stream between the four kernels (mamba2_ssd_forward_profile).
+    stage_sum = [0.0] * 4
+    for _ in range(args.steps):
+        ms4 = m2.mamba2_ssd_forward_profile(dims, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"],
+                                            g["init_state"], y, fin, ws, need, stream)
+        stage_sum = [a + b for a, b in zip(stage_sum, ms4)]
+    stage_ms = {s: stage_sum[i] / args.steps for i, s in enumerate(STAGES)}
     model = stage_model(w)
     dom = max(STAGES, key=lambda s: stage_ms[s])
     dm = model[dom]
@@ -159,6 +164,20 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_tokens)
     print(json.dumps(out), flush=True)
+
+
+def copy_probe(mib):
+    """A plain device-to-device copy of known size, used to calibrate the HBM
+    byte counters (each launch reads and writes `mib` MiB)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "launches": 5}), flush=True)
 
 
 def cpu_baseline(inp, w, tokens_per_head):

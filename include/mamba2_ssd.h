@@ -168,6 +168,19 @@ int mamba2_ssd_forward(const mamba2_dims* dims, const void* x, const void* dt,
                        const float* init_state, void* y, float* final_state,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Same as mamba2_ssd_forward, then waits for the work to finish and writes
+ * the device time of each stage in milliseconds to stage_ms[0..3]
+ * (chunk_cumsum, chunk_state, state_passing, chunk_scan), measured with HIP
+ * events recorded on `stream` between the launches.  For measurement only:
+ * it creates and destroys five events and blocks the calling thread.
+ */
+int mamba2_ssd_forward_profile(const mamba2_dims* dims, const void* x, const void* dt,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const float* init_state, void* y, float* final_state,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               float* stage_ms);
+
 /* Static description of a status code. */
 const char* mamba2_status_string(int status);
 

@@ -7,7 +7,8 @@ current torch stream into a ``hipStream_t``.  The functions keep the C names:
 
     mamba2_validate, mamba2_chunk_cumsum, mamba2_chunk_state,
     mamba2_state_passing, mamba2_chunk_scan, mamba2_ssd_workspace_bytes,
-    mamba2_ssd_forward, mamba2_status_string, mamba2_last_error
+    mamba2_ssd_forward, mamba2_ssd_forward_profile, mamba2_status_string,
+    mamba2_last_error
 
 plus ``make_dims`` and ``ssd_forward`` (allocates outputs and workspace with
 torch, then calls ``mamba2_ssd_forward``).  Importing fails loudly when the
@@ -38,7 +39,7 @@ MAMBA2_DTYPE_BF16 = 1
 EXPORTS = (
     "mamba2_validate", "mamba2_chunk_cumsum", "mamba2_chunk_state", "mamba2_state_passing",
     "mamba2_chunk_scan", "mamba2_ssd_workspace_bytes", "mamba2_ssd_forward",
-    "mamba2_status_string", "mamba2_last_error",
+    "mamba2_ssd_forward_profile", "mamba2_status_string", "mamba2_last_error",
 )
 
 
@@ -75,6 +76,8 @@ def _load():
         "mamba2_chunk_scan": ([D, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "mamba2_ssd_workspace_bytes": ([D], ctypes.c_size_t),
         "mamba2_ssd_forward": ([D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P], ctypes.c_int),
+        "mamba2_ssd_forward_profile": ([D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
+                                        ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
         "mamba2_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "mamba2_last_error": ([], ctypes.c_char_p),
     }
@@ -169,6 +172,19 @@ def mamba2_ssd_forward(dims, x, dt, A, B, C, D, init_state, y, final_state, work
                                    _ptr(C), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
                                    _ptr(workspace), int(workspace_bytes), _stream(stream)),
            "mamba2_ssd_forward")
+
+
+def mamba2_ssd_forward_profile(dims, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                               workspace_bytes, stream=None):
+    """Runs mamba2_ssd_forward, waits, and returns the four stage durations in ms
+    (chunk_cumsum, chunk_state, state_passing, chunk_scan)."""
+    ms = (ctypes.c_float * 4)()
+    _check(_lib.mamba2_ssd_forward_profile(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A),
+                                           _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), _ptr(y),
+                                           _ptr(final_state), _ptr(workspace),
+                                           int(workspace_bytes), _stream(stream), ms),
+           "mamba2_ssd_forward_profile")
+    return [float(v) for v in ms]
 
 
 def ssd_forward(x, dt, A, B, C, D=None, init_state=None, *, chunk_size=256, workspace=None,

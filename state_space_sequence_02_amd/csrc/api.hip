@@ -110,23 +110,89 @@ int hip_status(hipError_t e, const char* where) {
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Workspace of the fused forward: dA_cs and dt_T [B,H,nc,Q] f32, the per-chunk
+// states [B,nc,H,P,N] f32, and (grouped path) the chunk-start states as bf16.
 struct Workspace {
-  size_t cs_bytes, st_bytes, total;
+  bool grouped;
+  size_t cs_bytes, st_bytes, hst_bytes, total;
 };
 
 Workspace plan(const m2::Dims& d) {
   Workspace w;
+  w.grouped = m2::grouped_scan_supported(d);
   w.cs_bytes = round256((size_t)(d.B * d.H * d.nc * d.Q) * sizeof(float));
   w.st_bytes = round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * sizeof(float));
-  w.total = 2 * w.cs_bytes + w.st_bytes;
+  w.hst_bytes = w.grouped ? round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * 2) : 0;
+  w.total = 2 * w.cs_bytes + w.st_bytes + w.hst_bytes;
   return w;
 }
+
+// Enqueues the four stages; when `ev` is non-null, records ev[0..4] around them.
+int enqueue_forward(const m2::Dims& d, const void* x, const void* dt, const float* A,
+                    const void* B, const void* C, const float* D, const float* init_state,
+                    void* y, float* final_state, void* workspace, hipStream_t s,
+                    hipEvent_t* ev) {
+  const Workspace w = plan(d);
+  char* ws = (char*)workspace;
+  float* dA_cs = (float*)ws;
+  float* dt_T = (float*)(ws + w.cs_bytes);
+  float* states = (float*)(ws + 2 * w.cs_bytes);
+  void* hst = ws + 2 * w.cs_bytes + w.st_bytes;
+  hipError_t e = hipSuccess;
+  if (ev) e = hipEventRecord(ev[0], s);
+  if (e == hipSuccess) e = m2::launch_chunk_cumsum(d, dt, A, dA_cs, dt_T, s);
+  if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
+  if (ev) e = hipEventRecord(ev[1], s);
+  if (e == hipSuccess) e = m2::launch_chunk_state(d, x, B, dA_cs, dt_T, states, s);
+  if (e != hipSuccess) return hip_status(e, "chunk_state launch");
+  if (ev) e = hipEventRecord(ev[2], s);
+  if (e == hipSuccess)
+    e = w.grouped ? m2::launch_state_passing_bf16(d, states, dA_cs, init_state, hst, final_state, s)
+                  : m2::launch_state_passing(d, states, dA_cs, init_state, final_state, s);
+  if (e != hipSuccess) return hip_status(e, "state_passing launch");
+  if (ev) e = hipEventRecord(ev[3], s);
+  if (e == hipSuccess)
+    e = w.grouped ? m2::launch_chunk_scan_grouped(d, x, B, C, dA_cs, dt_T, hst, D, y, s)
+                  : m2::launch_chunk_scan(d, x, B, C, dA_cs, dt_T, states, D, y, s);
+  if (e != hipSuccess) return hip_status(e, "chunk_scan launch");
+  if (ev) e = hipEventRecord(ev[4], s);
+  return hip_status(e, "event record");
+}
+
+int check_forward_args(const mamba2_dims* dims, m2::Dims* d, const void* x, const void* dt,
+                       const float* A, const void* B, const void* C, const float* D,
+                       const float* init_state, void* y, float* final_state, void* workspace,
+                       size_t workspace_bytes);
 
 #define CHECK(expr)               \
   do {                            \
     const int rc_ = (expr);       \
     if (rc_ != MAMBA2_OK) return rc_; \
   } while (0)
+
+int check_forward_args(const mamba2_dims* dims, m2::Dims* d, const void* x, const void* dt,
+                       const float* A, const void* B, const void* C, const float* D,
+                       const float* init_state, void* y, float* final_state, void* workspace,
+                       size_t workspace_bytes) {
+  CHECK(validate(dims, d));
+  CHECK(need(x, "x"));
+  CHECK(need(dt, "dt"));
+  CHECK(need(A, "A"));
+  CHECK(need(B, "B"));
+  CHECK(need(C, "C"));
+  CHECK(maybe(D, "D"));
+  CHECK(maybe(init_state, "init_state"));
+  CHECK(need(y, "y"));
+  CHECK(maybe(final_state, "final_state"));
+  const Workspace w = plan(*d);
+  if (!workspace) return fail(MAMBA2_ERR_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(MAMBA2_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < w.total)
+    return fail(MAMBA2_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                w.total);
+  return MAMBA2_OK;
+}
 
 }  // namespace
 
@@ -204,36 +270,36 @@ int mamba2_ssd_forward(const mamba2_dims* dims, const void* x, const void* dt, c
                        void* y, float* final_state, void* workspace, size_t workspace_bytes,
                        void* stream) {
   m2::Dims d;
-  CHECK(validate(dims, &d));
-  CHECK(need(x, "x"));
-  CHECK(need(dt, "dt"));
-  CHECK(need(A, "A"));
-  CHECK(need(B, "B"));
-  CHECK(need(C, "C"));
-  CHECK(maybe(D, "D"));
-  CHECK(maybe(init_state, "init_state"));
-  CHECK(need(y, "y"));
-  CHECK(maybe(final_state, "final_state"));
-  const Workspace w = plan(d);
-  if (!workspace) return fail(MAMBA2_ERR_WORKSPACE, "workspace is NULL");
-  if (((uintptr_t)workspace & 255u) != 0)
-    return fail(MAMBA2_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  if (workspace_bytes < w.total)
-    return fail(MAMBA2_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
-                w.total);
-  char* ws = (char*)workspace;
-  float* dA_cs = (float*)ws;
-  float* dt_T = (float*)(ws + w.cs_bytes);
-  float* states = (float*)(ws + 2 * w.cs_bytes);
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = m2::launch_chunk_cumsum(d, dt, A, dA_cs, dt_T, s);
-  if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
-  e = m2::launch_chunk_state(d, x, B, dA_cs, dt_T, states, s);
-  if (e != hipSuccess) return hip_status(e, "chunk_state launch");
-  e = m2::launch_state_passing(d, states, dA_cs, init_state, final_state, s);
-  if (e != hipSuccess) return hip_status(e, "state_passing launch");
-  e = m2::launch_chunk_scan(d, x, B, C, dA_cs, dt_T, states, D, y, s);
-  return hip_status(e, "chunk_scan launch");
+  CHECK(check_forward_args(dims, &d, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                           workspace_bytes));
+  return enqueue_forward(d, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                         (hipStream_t)stream, nullptr);
+}
+
+int mamba2_ssd_forward_profile(const mamba2_dims* dims, const void* x, const void* dt,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const float* init_state, void* y, float* final_state,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               float* stage_ms) {
+  m2::Dims d;
+  CHECK(check_forward_args(dims, &d, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                           workspace_bytes));
+  if (!stage_ms) return fail(MAMBA2_ERR_NULL, "stage_ms is NULL");
+  hipEvent_t ev[5] = {};
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < 5 && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+  int rc = (e == hipSuccess) ? MAMBA2_OK : hip_status(e, "event create");
+  if (rc == MAMBA2_OK)
+    rc = enqueue_forward(d, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                         (hipStream_t)stream, ev);
+  if (rc == MAMBA2_OK) {
+    e = hipEventSynchronize(ev[4]);
+    for (int i = 0; i < 4 && e == hipSuccess; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+    rc = hip_status(e, "event timing");
+  }
+  for (int i = 0; i < 5; ++i)
+    if (ev[i]) (void)hipEventDestroy(ev[i]);
+  return rc;
 }
 
 const char* mamba2_status_string(int status) {

@@ -1,0 +1,370 @@
+// chunk_scan (compute_out), grouped variant used by the fused forward pass:
+// one workgroup serves one (batch, chunk, B/C group) and a run of that
+// group's heads.  The pages fuse the output stage so the chunk x chunk matrix
+// never reaches memory (devotd.net news item on the Mamba-2 CUDA Tile
+// forward-pass kernels, section 2); here it additionally never gets recomputed
+// per head: G^T = B C^T depends only on the group, so it is formed once per
+// workgroup, kept in fp32 accumulators, and reused by every head of the run,
+// each head applying its own decay mask (disconfirmai.com "Jane Street ML
+// Engineers Map Mamba-2 Recurrent State Computation to Tensor Cores with
+// cuTile", body: exponential row scaling keeps the matrix-product form).
+// The C operand of the carried-state contraction is likewise loaded once and
+// kept in registers for all heads.
+//
+// Per head the kernel streams only what is head-specific: the chunk-start
+// state (bfloat16, P x N) and the chunk's x rows (Q x P), plus the head's
+// cumulative sums.  They arrive through gfx950 direct-to-LDS loads into a
+// double buffer: while the waves compute head k from one buffer, head k+1's
+// bytes land in the other, so HBM stays busy with one workgroup per CU.
+// Both LDS tiles are XOR-swizzled in 16-byte units so the MFMA operand reads
+// (row reads of the state, transpose reads of x) spread over the LDS banks.
+//
+// Math, MFMA layouts, the transposed Y^T formulation and the row and K
+// permutations are those of the per-head chunk_scan kernel: Y^T[p, i] with
+// MFMA row m of p-tile pt standing for p = 16 (m/4) + 4 pt + m%4 (P = 64),
+// and the in-chunk product's K element e of lane group q standing for
+// j = 32 jp + 4q + e (e < 4) or 32 jp + 16 + 4q + (e - 4).
+#include "common.h"
+#include "launch.h"
+
+namespace m2 {
+
+namespace {
+
+template <int P, int Q, int N>
+struct GCfg {
+  static constexpr int QT = Q / 16, NW = Q / 32, PT = P / 16, NBLK = N / 64;
+  static constexpr int HS_BYTES = P * N * 2;     // state tile, bf16
+  static constexpr int XS_BYTES = Q * P * 2;     // x tile, bf16
+  static constexpr int CS_BYTES = Q * 4;         // cumulative sums (and dt), fp32
+  static constexpr int BUF = HS_BYTES + XS_BYTES + 2 * CS_BYTES;
+  static constexpr int SROW = 64 + 8;            // staging row stride (elements)
+  static constexpr int STG = 2 * Q * SROW * 2;   // B and C staging for G
+  static constexpr int LDS = BUF + (BUF > STG ? BUF : STG);
+  static constexpr int RLH = N / 8;              // 16-byte chunks per state row
+  static_assert(P == 64, "grouped chunk_scan is specialised for headdim 64");
+  static_assert(N == 64 || N == 128 || N == 256, "state size must be 64, 128 or 256");
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void* src, unsigned char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
+}
+
+// Chunk position of 16-byte chunk c of state row r (row length RLH chunks).
+template <int RLH>
+__device__ __forceinline__ int hswz(int r, int c) {
+  return c ^ (((r & 3) | (((r >> 4) & 3) << 2)) & (RLH - 1));
+}
+// Chunk position of 16-byte chunk c of x row r (8 chunks per row).
+__device__ __forceinline__ int xswz(int r, int c) { return c ^ (r & 7); }
+
+// Issues the direct-to-LDS loads of one head into buffer `buf`:
+// state rows (P x N bf16), x rows (Q x P bf16, rows past L clamped to L-1,
+// whose values are never used with a nonzero weight), cumulative sums, dt.
+template <int P, int Q, int N>
+__device__ __forceinline__ void load_head(unsigned char* buf, const bf16* __restrict__ hst,
+                                          const bf16* __restrict__ x,
+                                          const float* __restrict__ dA_cs,
+                                          const float* __restrict__ dt_T, int b, int c, int h,
+                                          int L, int H, int nc) {
+  using K = GCfg<P, Q, N>;
+  const int lane = lane_id();
+  const int w = wave_id();
+  // state: P*N/512 wave-loads of 64 chunks
+  const bf16* hsrc = hst + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+  constexpr int HI = P * N / 512 / K::NW;
+#pragma unroll
+  for (int i = 0; i < HI; ++i) {
+    const int k = w + K::NW * i;
+    const int s = k * 64 + lane;
+    const int r = s / K::RLH, pos = s % K::RLH;
+    const int cc = hswz<K::RLH>(r, pos);  // involution: position <-> chunk
+    dma16(hsrc + r * N + cc * 8, buf + k * 1024);
+  }
+  // x rows: Q/8 wave-loads of 8 rows
+  unsigned char* xs = buf + K::HS_BYTES;
+  constexpr int XI = Q / 8 / K::NW;
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int k = w + K::NW * i;
+    const int s = k * 64 + lane;
+    const int r = s >> 3, pos = s & 7;
+    int64_t t = (int64_t)c * Q + r;
+    if (t > L - 1) t = L - 1;
+    dma16(x + (((int64_t)b * L + t) * H + h) * P + xswz(r, pos) * 8, xs + k * 1024);
+  }
+  // cumulative sums (wave 0) and dt (wave 1): Q/4 chunks each
+  unsigned char* cs = xs + K::XS_BYTES;
+  const int64_t cb = (((int64_t)b * H + h) * nc + c) * Q;
+  if (w < 2 && lane < Q / 4) {
+    const float* src = (w == 0 ? dA_cs : dt_T) + cb + lane * 4;
+    dma16(src, cs + w * K::CS_BYTES);
+  }
+}
+
+
+// Masked, decayed in-chunk contribution of one 16-row i-tile t (see the
+// per-head kernel): scales the carried-state part of Yt by 2^cs_i, then adds
+// sum over j-tiles 0..t of x^T (G^T * 2^(cs_i - cs_j) * dt_j, causal, + D on
+// the diagonal).  css/dts/Xs are this head's LDS tiles.
+template <int QT, bool REV, int P>
+__device__ __forceinline__ void finish_tile(const f32x4 (&Gs)[QT + 1], f32x4 (&Yt)[P / 16], int t,
+                                            const float* css, const float* dts,
+                                            const unsigned char* Xs, float Dh) {
+  constexpr int PT = P / 16;
+  const int lane = lane_id();
+  const int L16 = lane & 15, grp = lane >> 4;
+  const int i = 16 * t + L16;
+  const float csi = css[i];
+  const float sc = fast_exp2(csi);
+#pragma unroll
+  for (int pt = 0; pt < PT; ++pt) Yt[pt] *= sc;
+  // j-tile jt of the wave's first i-tile sits in slot jt, of its second i-tile
+  // in slot QT - jt; NG bounds the j-tiles either can have.
+  constexpr int NG = REV ? QT : QT / 2;
+#pragma unroll
+  for (int jp = 0; jp < (NG + 1) / 2; ++jp) {
+    if (2 * jp > t) break;
+    bf16x8 gm;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int jt = 2 * jp + half;
+      if (jt < NG && jt <= t) {
+        const f32x4 gt = Gs[REV ? QT - (jt < NG ? jt : 0) : (jt < NG ? jt : 0)];
+        const f32x4 cj = *(const f32x4*)(css + 16 * jt + 4 * grp);
+        const f32x4 dj = *(const f32x4*)(dts + 16 * jt + 4 * grp);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * jt + 4 * grp + r;
+          float gv = (j <= i) ? gt[r] * fast_exp2(csi - cj[r]) * dj[r] : 0.f;
+          if (j == i) gv += Dh;
+          gm[half * 4 + r] = f2bf(gv);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gm[half * 4 + r] = f2bf(0.f);
+      }
+    }
+    const int ra = 32 * jp + 4 * grp + (L16 >> 2), rb = ra + 16;
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+      const int p0 = 4 * PT * (L16 & 3) + 4 * pt;
+      const int ch = p0 >> 3, off = (p0 & 7) * 2;
+      const bf16* pa = (const bf16*)(Xs + ra * (P * 2) + (xswz(ra, ch) << 4) + off);
+      const bf16* pb = (const bf16*)(Xs + rb * (P * 2) + (xswz(rb, ch) << 4) + off);
+      const bf16x8 xop = cat(lds_read_tr(pa), lds_read_tr(pb));
+      Yt[pt] = mfma16x16x32(xop, gm, Yt[pt]);
+    }
+  }
+}
+
+// Stores one i-tile of Y^T: lane (i, group q) holds p = 4 PT q .. 4 PT q + 4 PT - 1.
+template <int P>
+__device__ __forceinline__ void store_tile(const f32x4 (&Yt)[P / 16], int t, bf16* __restrict__ y,
+                                           int64_t ybase, int H, int64_t valid) {
+  constexpr int PT = P / 16;
+  const int lane = lane_id();
+  const int L16 = lane & 15, grp = lane >> 4;
+  const int i = 16 * t + L16;
+  if (i < valid) {
+    bf16* dst = y + (ybase + (int64_t)i * H) * P + 4 * PT * grp;
+#pragma unroll
+    for (int pt = 0; pt < PT; pt += 2) {
+      bf16x8 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        o[r] = f2bf(Yt[pt][r]);
+        o[4 + r] = f2bf(Yt[pt + 1][r]);
+      }
+      *(bf16x8*)(dst + 4 * pt) = o;
+    }
+  }
+}
+
+template <int P, int Q, int N>
+__global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
+    const float* __restrict__ dA_cs, const float* __restrict__ dt_T,
+    const bf16* __restrict__ hst, const float* __restrict__ Dv, bf16* __restrict__ y, int L,
+    int H, int G, int nc, int hpw, int slices) {
+  using K = GCfg<P, Q, N>;
+  constexpr int QT = K::QT, PT = K::PT, NBLK = K::NBLK, SROW = K::SROW;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  bf16* Cs = (bf16*)(smem + K::BUF);  // phase-A staging aliases buffer 1
+  bf16* Bs = Cs + Q * SROW;
+
+  int bid = blockIdx.x;
+  const int slice = bid % slices;
+  bid /= slices;
+  const int g = bid % G;
+  bid /= G;
+  const int c = bid % nc;
+  const int b = bid / nc;
+  const int HG = H / G;
+  const int h0 = g * HG + slice * hpw;
+  const int nh = min(hpw, HG - slice * hpw);
+
+  const int tid = threadIdx.x;
+  constexpr int nthr = Q * 2;
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int L16 = lane & 15, grp = lane >> 4;
+  const int t0 = w, t1 = QT - 1 - w;
+  const int64_t tok0 = (int64_t)c * Q;
+
+  // Head 0's bytes start flowing while G is formed.
+  load_head<P, Q, N>(smem, hst, x, dA_cs, dt_T, b, c, h0, L, H, nc);
+
+  // ---- Phase A: G^T tiles of this wave's two i-tiles, and its C operands.
+  // G^T tiles: j-tile jt of i-tile t0 in slot jt (jt <= t0), of i-tile t1 in
+  // slot QT - jt (jt <= t1); together exactly QT + 1 slots.
+  f32x4 Gs[QT + 1];
+#pragma unroll
+  for (int a = 0; a <= QT; ++a) Gs[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 C0[NBLK][2], C1[NBLK][2];
+#pragma unroll
+  for (int nb = 0; nb < NBLK; ++nb) {
+    __syncthreads();
+    for (int idx = tid; idx < Q * 8; idx += nthr) {
+      const int r = idx >> 3, c8 = (idx & 7) * 8;
+      const int64_t t = tok0 + r;
+      bf16x8 vc, vb;
+      if (t < L) {
+        const int64_t off = (((int64_t)b * L + t) * G + g) * N + nb * 64 + c8;
+        vc = *(const bf16x8*)(Cm + off);
+        vb = *(const bf16x8*)(Bm + off);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vc[e] = vb[e] = f2bf(0.f);
+      }
+      *(bf16x8*)(Cs + r * SROW + c8) = vc;
+      *(bf16x8*)(Bs + r * SROW + c8) = vb;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int koff = kk * 32 + grp * 8;
+      const bf16x8 c0 = *(const bf16x8*)(Cs + (16 * t0 + L16) * SROW + koff);
+      const bf16x8 c1 = *(const bf16x8*)(Cs + (16 * t1 + L16) * SROW + koff);
+      C0[nb][kk] = c0;
+      C1[nb][kk] = c1;
+#pragma unroll
+      for (int jt = 0; jt < QT; ++jt) {
+        if (jt <= t1) {
+          const bf16x8 bop = *(const bf16x8*)(Bs + (16 * jt + L16) * SROW + koff);
+          if (jt < QT / 2 && jt <= t0) Gs[jt] = mfma16x16x32(bop, c0, Gs[jt]);
+          Gs[QT - jt] = mfma16x16x32(bop, c1, Gs[QT - jt]);
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // ---- Phase B: heads.
+  for (int k = 0; k < nh; ++k) {
+    const int h = h0 + k;
+    unsigned char* cur = smem + (k & 1) * K::BUF;
+    if (k + 1 < nh)
+      load_head<P, Q, N>(smem + ((k + 1) & 1) * K::BUF, hst, x, dA_cs, dt_T, b, c, h + 1, L, H, nc);
+    const unsigned char* Hs = cur;
+    const unsigned char* Xs = cur + K::HS_BYTES;
+    const float* css = (const float*)(Xs + K::XS_BYTES);
+    const float* dts = css + Q;
+
+    f32x4 Y[2][PT];
+#pragma unroll
+    for (int a = 0; a < PT; ++a) Y[0][a] = Y[1][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // carried-state term: Y^T[p, i] = sum_n h[p, n] C[i, n]
+#pragma unroll
+    for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          const int r = 16 * (L16 >> 2) + 4 * pt + (L16 & 3);
+          const int cc = nb * 8 + kk * 4 + grp;
+          const bf16x8 hop = *(const bf16x8*)(Hs + r * (N * 2) + (hswz<K::RLH>(r, cc) << 4));
+          Y[0][pt] = mfma16x16x32(hop, C0[nb][kk], Y[0][pt]);
+          Y[1][pt] = mfma16x16x32(hop, C1[nb][kk], Y[1][pt]);
+        }
+    const float Dh = Dv ? Dv[h] : 0.f;
+    finish_tile<QT, false, P>(Gs, Y[0], t0, css, dts, Xs, Dh);
+    finish_tile<QT, true, P>(Gs, Y[1], t1, css, dts, Xs, Dh);
+
+    __builtin_amdgcn_s_waitcnt(0);  // next head's bytes have landed (and older stores drained)
+    const int64_t valid = L - tok0;
+    store_tile<P>(Y[0], t0, y, ((int64_t)b * L + tok0) * H + h, H, valid);
+    store_tile<P>(Y[1], t1, y, ((int64_t)b * L + tok0) * H + h, H, valid);
+    __syncthreads();
+  }
+}
+
+int cu_count() {
+  static const int n = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    return v;
+  }();
+  return n;
+}
+
+template <int P, int Q, int N>
+hipError_t launch_grouped(const Dims& d, const void* x, const void* B, const void* C,
+                          const float* dA_cs, const float* dt_T, const void* hst, const float* D,
+                          void* y, hipStream_t s) {
+  using K = GCfg<P, Q, N>;
+  auto kern = chunk_scan_grouped_kernel<P, Q, N>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS);
+  if (attr != hipSuccess) return attr;
+  // Heads per workgroup: enough workgroups to cover every CU once, as many
+  // heads per workgroup as that allows (G^T is formed once per workgroup).
+  const int64_t HG = d.H / d.G;
+  int64_t hpw = (d.B * d.nc * d.H) / cu_count();
+  if (hpw < 1) hpw = 1;
+  if (hpw > HG) hpw = HG;
+  const int64_t slices = (HG + hpw - 1) / hpw;
+  hpw = (HG + slices - 1) / slices;  // balance the slices
+  const int64_t grid = d.B * d.nc * d.G * slices;
+  kern<<<(unsigned)grid, Q * 2, K::LDS, s>>>(
+      (const bf16*)x, (const bf16*)B, (const bf16*)C, dA_cs, dt_T, (const bf16*)hst, D,
+      (bf16*)y, (int)d.L, (int)d.H, (int)d.G, (int)d.nc, (int)hpw, (int)slices);
+  return hipGetLastError();
+}
+
+template <int Q>
+hipError_t launch_grouped_n(const Dims& d, const void* x, const void* B, const void* C,
+                            const float* dA_cs, const float* dt_T, const void* hst,
+                            const float* D, void* y, hipStream_t s) {
+  switch (d.N) {
+    case 64: return launch_grouped<64, Q, 64>(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
+    case 128: return launch_grouped<64, Q, 128>(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
+    case 256: return launch_grouped<64, Q, 256>(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool grouped_scan_supported(const Dims& d) {
+  return d.bf16 && d.P == 64 && (d.N == 64 || d.N == 128 || d.N == 256) &&
+         (d.Q == 64 || d.Q == 128 || d.Q == 256);
+}
+
+hipError_t launch_chunk_scan_grouped(const Dims& d, const void* x, const void* B, const void* C,
+                                     const float* dA_cs, const float* dt_T, const void* hst,
+                                     const float* D, void* y, hipStream_t s) {
+  switch (d.Q) {
+    case 64: return launch_grouped_n<64>(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
+    case 128: return launch_grouped_n<128>(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
+    case 256: return launch_grouped_n<256>(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace m2

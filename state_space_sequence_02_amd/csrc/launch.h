@@ -22,4 +22,15 @@ hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* B, const 
                              const float* dA_cs, const float* dt_T, const float* states,
                              const float* D, void* y, hipStream_t s);
 
+// Fused-forward variants: state_passing that leaves the chunk-start states as
+// bfloat16 in a separate buffer (the float32 per-chunk states are read once),
+// and the grouped chunk_scan that consumes them.
+hipError_t launch_state_passing_bf16(const Dims& d, const float* states, const float* dA_cs,
+                                     const float* init, void* hst, float* final_state,
+                                     hipStream_t s);
+bool grouped_scan_supported(const Dims& d);
+hipError_t launch_chunk_scan_grouped(const Dims& d, const void* x, const void* B, const void* C,
+                                     const float* dA_cs, const float* dt_T, const void* hst,
+                                     const float* D, void* y, hipStream_t s);
+
 }  // namespace m2

@@ -21,11 +21,14 @@ constexpr int kDepth = 16;
 constexpr int kThreads = 256;
 
 // V is float4 when P*N is a multiple of 4 (every bfloat16 size), else float.
+// With `hst` non-null (float4 only) the chunk-start states go there as
+// bfloat16 (round to nearest even) and `states` is only read; otherwise they
+// overwrite `states` in place.
 template <typename V>
 __global__ void __launch_bounds__(kThreads) state_passing_kernel(
     float* __restrict__ states, const float* __restrict__ dA_cs, const float* __restrict__ init,
-    float* __restrict__ final_state, int64_t H, int64_t PNv, int64_t blocks_per_head, int nc,
-    int Q) {
+    float* __restrict__ final_state, bf16* __restrict__ hst, int64_t H, int64_t PNv,
+    int64_t blocks_per_head, int nc, int Q) {
   const int64_t bh = (int64_t)blockIdx.x / blocks_per_head;  // b * H + h
   const int64_t gid = ((int64_t)blockIdx.x % blocks_per_head) * kThreads + threadIdx.x;
   if (gid >= PNv) return;
@@ -51,7 +54,18 @@ __global__ void __launch_bounds__(kThreads) state_passing_kernel(
         if (c + kDepth < nc)
           buf[k] = __builtin_nontemporal_load(base + (int64_t)(c + kDepth) * chunk_stride);
         const float decay = exp2f(cs_last[(int64_t)c * Q]);
-        __builtin_nontemporal_store(run, base + (int64_t)c * chunk_stride);
+        if constexpr (sizeof(V) == 16) {
+          if (hst) {
+            bf16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = f2bf(run[e]);
+            *((bf16x4*)hst + (b * nc * H + h) * PNv + gid + (int64_t)c * chunk_stride) = o;
+          } else {
+            __builtin_nontemporal_store(run, base + (int64_t)c * chunk_stride);
+          }
+        } else {
+          __builtin_nontemporal_store(run, base + (int64_t)c * chunk_stride);
+        }
         run = decay * run + cur;
       }
     }
@@ -67,12 +81,24 @@ hipError_t launch_state_passing(const Dims& d, float* states, const float* dA_cs
   if (PN % 4 == 0) {
     const int64_t PNv = PN / 4, bph = (PNv + kThreads - 1) / kThreads;
     state_passing_kernel<f32x4><<<(unsigned)(d.B * d.H * bph), kThreads, 0, s>>>(
-        states, dA_cs, init, final_state, d.H, PNv, bph, (int)d.nc, (int)d.Q);
+        states, dA_cs, init, final_state, nullptr, d.H, PNv, bph, (int)d.nc, (int)d.Q);
   } else {
     const int64_t bph = (PN + kThreads - 1) / kThreads;
     state_passing_kernel<float><<<(unsigned)(d.B * d.H * bph), kThreads, 0, s>>>(
-        states, dA_cs, init, final_state, d.H, PN, bph, (int)d.nc, (int)d.Q);
+        states, dA_cs, init, final_state, nullptr, d.H, PN, bph, (int)d.nc, (int)d.Q);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_state_passing_bf16(const Dims& d, const float* states, const float* dA_cs,
+                                     const float* init, void* hst, float* final_state,
+                                     hipStream_t s) {
+  const int64_t PN = d.P * d.N;
+  if (PN % 4 != 0) return hipErrorInvalidValue;
+  const int64_t PNv = PN / 4, bph = (PNv + kThreads - 1) / kThreads;
+  state_passing_kernel<f32x4><<<(unsigned)(d.B * d.H * bph), kThreads, 0, s>>>(
+      const_cast<float*>(states), dA_cs, init, final_state, (bf16*)hst, d.H, PNv, bph,
+      (int)d.nc, (int)d.Q);
   return hipGetLastError();
 }
 

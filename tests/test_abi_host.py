@@ -72,10 +72,15 @@ def test_workspace_bytes():
     nc = 256
     cs = 1 * 32 * nc * 256 * 4
     st = 1 * nc * 32 * 64 * 256 * 4
-    assert m2.mamba2_ssd_workspace_bytes(d) == 2 * cs + st
+    # headdim 64 with dstate 256 runs the grouped output stage, which also keeps
+    # the chunk-start states as bfloat16
+    assert m2.mamba2_ssd_workspace_bytes(d) == 2 * cs + st + st // 2
     # ragged sequence rounds chunks up
     d2 = _dims(seqlen=1000)
-    assert m2.mamba2_ssd_workspace_bytes(d2) == 2 * (8 * 4 * 256 * 4) + 4 * 8 * 64 * 64 * 4
+    assert m2.mamba2_ssd_workspace_bytes(d2) == 2 * (8 * 4 * 256 * 4) + 4 * 8 * 64 * 64 * 6
+    # headdim 32 uses the per-head output stage on float32 states only
+    d3 = _dims(seqlen=1000, headdim=32)
+    assert m2.mamba2_ssd_workspace_bytes(d3) == 2 * (8 * 4 * 256 * 4) + 4 * 8 * 32 * 64 * 4
 
 
 def test_status_strings():

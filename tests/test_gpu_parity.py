@@ -263,3 +263,31 @@ def test_bad_workspace_is_rejected_without_launch(m2):
     assert ei.value.status == m2.MAMBA2_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert torch.all(y == 3.0)
+
+
+# The fused forward's grouped output stage serves several heads per workgroup;
+# these shapes give several head slices per group, a short last slice, G > 1,
+# every state size it supports, and a ragged last chunk.
+GROUPED = [
+    _custom(name="grp_N64_slices", batch=1, seqlen=16384 - 100, nheads=10, headdim=64, dstate=64,
+            ngroups=2, chunk_size=256, init_state=True, seed=41),
+    _custom(name="grp_N256_slices", batch=1, seqlen=8192, nheads=16, headdim=64, dstate=256,
+            ngroups=1, chunk_size=256, seed=42),
+    _custom(name="grp_N128_q64", batch=2, seqlen=4096 + 33, nheads=8, headdim=64, dstate=128,
+            ngroups=4, chunk_size=64, init_state=True, seed=43),
+    _custom(name="grp_N256_q128", batch=1, seqlen=6000, nheads=12, headdim=64, dstate=256,
+            ngroups=3, chunk_size=128, seed=44),
+]
+
+
+@pytest.mark.parametrize("w", GROUPED, ids=lambda w: w.name)
+def test_forward_grouped_heads(m2, w):
+    say(f"[grouped] {w}")
+    inp = ssd_inputs.make_inputs(w)
+    o = oracle_inputs(inp)
+    y, fin = run_forward(m2, to_gpu(inp), w.chunk_size)
+    oy, ofin, _ = oracle.ssd_recurrence(o["x"], o["dt"], o["A"], o["B"], o["C"], o["D"],
+                                        o["init_state"], chunk_size=w.chunk_size)
+    ey, ef = normwise(f64(y), oy), normwise(f64(fin), ofin)
+    say(f"  y {ey:.3e} final {ef:.3e}")
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
