@@ -13,6 +13,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -157,13 +158,47 @@ def main():
                    "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
                    "chunk_size": w.chunk_size, "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
-                     "unit": unit, "frac": achieved / peak, "traffic": None,
+                     "unit": unit, "frac": achieved / peak,
+                     "traffic": profiled_traffic(w.name, dom),
                      "algorithmic_bytes": dm["bytes"], "algorithmic_flops": dm["flops"]},
         "stages": stages,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_tokens)
     print(json.dumps(out), flush=True)
+
+
+def csrc_digest():
+    """sha256 over the HIP sources (file names and bytes, in name order)."""
+    import hashlib
+    d = os.path.join(ROOT, "state_space_sequence_02_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload, stage):
+    """HBM bytes per launch of `stage` from the committed rocprofv3 summary of
+    this workload (FETCH_SIZE and WRITE_SIZE, each scaled by the copy-kernel
+    calibration), or None when there is none or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"ssd_forward_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"csrc-sha256: ([0-9a-f]{64})", text)
+    if not m or m.group(1) != csrc_digest():
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 8 and cells[0].startswith(stage):
+            try:
+                return float(cells[5]) * 1e6
+            except ValueError:
+                return None
+    return None
 
 
 def copy_probe(mib):

@@ -143,7 +143,9 @@ int enqueue_forward(const m2::Dims& d, const void* x, const void* dt, const floa
   if (e == hipSuccess) e = m2::launch_chunk_cumsum(d, dt, A, dA_cs, dt_T, s);
   if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
   if (ev) e = hipEventRecord(ev[1], s);
-  if (e == hipSuccess) e = m2::launch_chunk_state(d, x, B, dA_cs, dt_T, states, s);
+  if (e == hipSuccess)
+    e = m2::grouped_state_supported(d) ? m2::launch_chunk_state_grouped(d, x, B, dA_cs, dt_T, states, s)
+                                       : m2::launch_chunk_state(d, x, B, dA_cs, dt_T, states, s);
   if (e != hipSuccess) return hip_status(e, "chunk_state launch");
   if (ev) e = hipEventRecord(ev[2], s);
   if (e == hipSuccess)

@@ -108,10 +108,13 @@ __device__ __forceinline__ void load_head(unsigned char* buf, const bf16* __rest
 // Masked, decayed in-chunk contribution of one 16-row i-tile t (see the
 // per-head kernel): scales the carried-state part of Yt by 2^cs_i, then adds
 // sum over j-tiles 0..t of x^T (G^T * 2^(cs_i - cs_j) * dt_j, causal, + D on
-// the diagonal).  css/dts/Xs are this head's LDS tiles.
+// the diagonal).  lws[j] = cs_j - log2(dt_j) folds dt_j into the exponent
+// (dt_j = 0 gives +inf and a zero weight), so a tile strictly below the
+// diagonal costs one subtract, one exp2 and one multiply per element; only
+// the diagonal tile is masked.  css/lws/Xs are this head's LDS tiles.
 template <int QT, bool REV, int P>
 __device__ __forceinline__ void finish_tile(const f32x4 (&Gs)[QT + 1], f32x4 (&Yt)[P / 16], int t,
-                                            const float* css, const float* dts,
+                                            const float* css, const float* lws,
                                             const unsigned char* Xs, float Dh) {
   constexpr int PT = P / 16;
   const int lane = lane_id();
@@ -131,14 +134,19 @@ __device__ __forceinline__ void finish_tile(const f32x4 (&Gs)[QT + 1], f32x4 (&Y
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int jt = 2 * jp + half;
-      if (jt < NG && jt <= t) {
-        const f32x4 gt = Gs[REV ? QT - (jt < NG ? jt : 0) : (jt < NG ? jt : 0)];
-        const f32x4 cj = *(const f32x4*)(css + 16 * jt + 4 * grp);
-        const f32x4 dj = *(const f32x4*)(dts + 16 * jt + 4 * grp);
+      const int slot = REV ? QT - (jt < NG ? jt : 0) : (jt < NG ? jt : 0);
+      if (jt < NG && jt < t) {
+        const f32x4 gt = Gs[slot];
+        const f32x4 lw = *(const f32x4*)(lws + 16 * jt + 4 * grp);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gm[half * 4 + r] = f2bf(gt[r] * fast_exp2(csi - lw[r]));
+      } else if (jt < NG && jt == t) {
+        const f32x4 gt = Gs[slot];
+        const f32x4 lw = *(const f32x4*)(lws + 16 * jt + 4 * grp);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * jt + 4 * grp + r;
-          float gv = (j <= i) ? gt[r] * fast_exp2(csi - cj[r]) * dj[r] : 0.f;
+          float gv = (j <= i) ? gt[r] * fast_exp2(csi - lw[r]) : 0.f;
           if (j == i) gv += Dh;
           gm[half * 4 + r] = f2bf(gv);
         }
@@ -290,6 +298,12 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
           Y[0][pt] = mfma16x16x32(hop, C0[nb][kk], Y[0][pt]);
           Y[1][pt] = mfma16x16x32(hop, C1[nb][kk], Y[1][pt]);
         }
+    // dt_j -> cs_j - log2(dt_j), in place (the in-chunk weights' exponent offset)
+    if (tid < Q) {
+      float* lw = (float*)dts;
+      lw[tid] = css[tid] - __builtin_amdgcn_logf(lw[tid]);
+    }
+    __syncthreads();
     const float Dh = Dv ? Dv[h] : 0.f;
     finish_tile<QT, false, P>(Gs, Y[0], t0, css, dts, Xs, Dh);
     finish_tile<QT, true, P>(Gs, Y[1], t1, css, dts, Xs, Dh);

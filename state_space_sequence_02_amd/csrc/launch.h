@@ -29,6 +29,10 @@ hipError_t launch_state_passing_bf16(const Dims& d, const float* states, const f
                                      const float* init, void* hst, float* final_state,
                                      hipStream_t s);
 bool grouped_scan_supported(const Dims& d);
+bool grouped_state_supported(const Dims& d);
+hipError_t launch_chunk_state_grouped(const Dims& d, const void* x, const void* B,
+                                      const float* dA_cs, const float* dt_T, float* states,
+                                      hipStream_t s);
 hipError_t launch_chunk_scan_grouped(const Dims& d, const void* x, const void* B, const void* C,
                                      const float* dA_cs, const float* dt_T, const void* hst,
                                      const float* D, void* y, hipStream_t s);

@@ -98,10 +98,13 @@ def test_stages_and_forward(m2, w):
     say(f"  errors {errs}")
     for k, e in errs.items():
         assert e <= tol, (k, e)
-    # the fused entry point gives the same numbers as the chained stages
+    # the fused entry point (its own kernels for some sizes) agrees with the
+    # chained stages and with the oracle
     y2, fin2 = run_forward(m2, g, w.chunk_size)
-    assert torch.equal(y2, y)
-    assert torch.equal(fin2, fin)
+    assert normwise(f64(y2), f64(y)) <= tol
+    assert normwise(f64(fin2), f64(fin)) <= tol
+    assert normwise(f64(y2), oy) <= tol
+    assert normwise(f64(fin2), ofin) <= tol
 
 
 @pytest.mark.parametrize("w", [_wl("small_L1k_N64"), _wl("tiny_fp32_L256_N16"), EDGE[0], EDGE[3]],
