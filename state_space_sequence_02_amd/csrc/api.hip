@@ -226,8 +226,11 @@ int mamba2_chunk_state(const mamba2_dims* dims, const void* x, const void* B, co
   CHECK(need(dA_cs, "dA_cs"));
   CHECK(need(dt_T, "dt_T"));
   CHECK(need(states, "states"));
-  return hip_status(m2::launch_chunk_state(d, x, B, dA_cs, dt_T, states, (hipStream_t)stream),
-                    "chunk_state launch");
+  const hipError_t e =
+      m2::grouped_state_supported(d)
+          ? m2::launch_chunk_state_grouped(d, x, B, dA_cs, dt_T, states, (hipStream_t)stream)
+          : m2::launch_chunk_state(d, x, B, dA_cs, dt_T, states, (hipStream_t)stream);
+  return hip_status(e, "chunk_state launch");
 }
 
 int mamba2_state_passing(const mamba2_dims* dims, float* states, const float* dA_cs,

@@ -46,12 +46,6 @@ struct GCfg {
   static_assert(N == 64 || N == 128 || N == 256, "state size must be 64, 128 or 256");
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void dma16(const void* src, unsigned char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
-}
-
 // Chunk position of 16-byte chunk c of state row r (row length RLH chunks).
 template <int RLH>
 __device__ __forceinline__ int hswz(int r, int c) {
@@ -64,7 +58,7 @@ __device__ __forceinline__ int xswz(int r, int c) { return c ^ (r & 7); }
 // state rows (P x N bf16), x rows (Q x P bf16, rows past L clamped to L-1,
 // whose values are never used with a nonzero weight), cumulative sums, dt.
 template <int P, int Q, int N>
-__device__ __forceinline__ void load_head(unsigned char* buf, const bf16* __restrict__ hst,
+__device__ __forceinline__ void load_head(uint32_t buf, const bf16* __restrict__ hst,
                                           const bf16* __restrict__ x,
                                           const float* __restrict__ dA_cs,
                                           const float* __restrict__ dt_T, int b, int c, int h,
@@ -84,7 +78,7 @@ __device__ __forceinline__ void load_head(unsigned char* buf, const bf16* __rest
     dma16(hsrc + r * N + cc * 8, buf + k * 1024);
   }
   // x rows: Q/8 wave-loads of 8 rows
-  unsigned char* xs = buf + K::HS_BYTES;
+  const uint32_t xs = buf + K::HS_BYTES;
   constexpr int XI = Q / 8 / K::NW;
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
@@ -96,7 +90,7 @@ __device__ __forceinline__ void load_head(unsigned char* buf, const bf16* __rest
     dma16(x + (((int64_t)b * L + t) * H + h) * P + xswz(r, pos) * 8, xs + k * 1024);
   }
   // cumulative sums (wave 0) and dt (wave 1): Q/4 chunks each
-  unsigned char* cs = xs + K::XS_BYTES;
+  const uint32_t cs = xs + K::XS_BYTES;
   const int64_t cb = (((int64_t)b * H + h) * nc + c) * Q;
   if (w < 2 && lane < Q / 4) {
     const float* src = (w == 0 ? dA_cs : dt_T) + cb + lane * 4;
@@ -223,7 +217,8 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
   const int64_t tok0 = (int64_t)c * Q;
 
   // Head 0's bytes start flowing while G is formed.
-  load_head<P, Q, N>(smem, hst, x, dA_cs, dt_T, b, c, h0, L, H, nc);
+  const uint32_t sbase = lds_addr(smem);
+  load_head<P, Q, N>(sbase, hst, x, dA_cs, dt_T, b, c, h0, L, H, nc);
 
   // ---- Phase A: G^T tiles of this wave's two i-tiles, and its C operands.
   // G^T tiles: j-tile jt of i-tile t0 in slot jt (jt <= t0), of i-tile t1 in
@@ -234,7 +229,7 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
   bf16x8 C0[NBLK][2], C1[NBLK][2];
 #pragma unroll
   for (int nb = 0; nb < NBLK; ++nb) {
-    __syncthreads();
+    lds_barrier();
     for (int idx = tid; idx < Q * 8; idx += nthr) {
       const int r = idx >> 3, c8 = (idx & 7) * 8;
       const int64_t t = tok0 + r;
@@ -250,7 +245,7 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
       *(bf16x8*)(Cs + r * SROW + c8) = vc;
       *(bf16x8*)(Bs + r * SROW + c8) = vb;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int koff = kk * 32 + grp * 8;
@@ -269,14 +264,14 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  lds_barrier();
 
   // ---- Phase B: heads.
   for (int k = 0; k < nh; ++k) {
     const int h = h0 + k;
     unsigned char* cur = smem + (k & 1) * K::BUF;
     if (k + 1 < nh)
-      load_head<P, Q, N>(smem + ((k + 1) & 1) * K::BUF, hst, x, dA_cs, dt_T, b, c, h + 1, L, H, nc);
+      load_head<P, Q, N>(sbase + ((k + 1) & 1) * K::BUF, hst, x, dA_cs, dt_T, b, c, h + 1, L, H, nc);
     const unsigned char* Hs = cur;
     const unsigned char* Xs = cur + K::HS_BYTES;
     const float* css = (const float*)(Xs + K::XS_BYTES);
@@ -303,7 +298,7 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
       float* lw = (float*)dts;
       lw[tid] = css[tid] - __builtin_amdgcn_logf(lw[tid]);
     }
-    __syncthreads();
+    lds_barrier();  // weights visible; next head's loads stay in flight
     const float Dh = Dv ? Dv[h] : 0.f;
     finish_tile<QT, false, P>(Gs, Y[0], t0, css, dts, Xs, Dh);
     finish_tile<QT, true, P>(Gs, Y[1], t1, css, dts, Xs, Dh);
@@ -312,7 +307,7 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
     const int64_t valid = L - tok0;
     store_tile<P>(Y[0], t0, y, ((int64_t)b * L + tok0) * H + h, H, valid);
     store_tile<P>(Y[1], t1, y, ((int64_t)b * L + tok0) * H + h, H, valid);
-    __syncthreads();
+    lds_barrier();
   }
 }
 

@@ -42,17 +42,11 @@ struct SCfg {
   static_assert(N == 64 || N == 128 || N == 256, "state size must be 64, 128 or 256");
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void dma16(const void* src, unsigned char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
-}
-
 // Position of 16-byte chunk c in x row r (8 chunks per row); an involution.
 __device__ __forceinline__ int xswz(int r, int c) { return c ^ (r & 7); }
 
 template <int P, int Q, int N>
-__device__ __forceinline__ void load_x(unsigned char* buf, const bf16* __restrict__ x,
+__device__ __forceinline__ void load_x(uint32_t buf, const bf16* __restrict__ x,
                                        const float* __restrict__ dA_cs,
                                        const float* __restrict__ dt_T, int b, int c, int h,
                                        int L, int H, int nc) {
@@ -69,7 +63,7 @@ __device__ __forceinline__ void load_x(unsigned char* buf, const bf16* __restric
     if (t > L - 1) t = L - 1;  // rows past L get w = 0 below
     dma16(x + (((int64_t)b * L + t) * H + h) * P + xswz(r, pos) * 8, buf + k * 1024);
   }
-  unsigned char* cs = buf + K::XS_BYTES;
+  const uint32_t cs = buf + K::XS_BYTES;
   const int64_t cb = (((int64_t)b * H + h) * nc + c) * Q;
   if (w < 2 && lane < Q / 4) dma16((w == 0 ? dA_cs : dt_T) + cb + lane * 4, cs + w * K::CS_BYTES);
 }
@@ -102,13 +96,14 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
   const int n0 = w * 16 * NTW;
   const int64_t tok0 = (int64_t)c * Q;
 
-  load_x<P, Q, N>(smem, x, dA_cs, dt_T, b, c, h0, L, H, nc);
+  const uint32_t sbase = lds_addr(smem);
+  load_x<P, Q, N>(sbase, x, dA_cs, dt_T, b, c, h0, L, H, nc);
 
   // ---- Phase A: B^T operands of this wave's columns, 64 time steps at a time.
   bf16x8 Bop[NTW][KS];
 #pragma unroll
   for (int jb = 0; jb < Q / 64; ++jb) {
-    __syncthreads();
+    lds_barrier();
     for (int idx = tid; idx < 64 * (N / 8); idx += K::NT) {
       const int r = idx / (N / 8), c8 = (idx % (N / 8)) * 8;
       const int64_t t = tok0 + jb * 64 + r;
@@ -121,7 +116,7 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
       }
       *(bf16x8*)(Bs + r * BROW + c8) = v;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int k0 = kk * 32 + grp * 8 + (L16 >> 2);
@@ -133,13 +128,13 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  lds_barrier();
 
   // ---- Phase B: heads.
   for (int k = 0; k < nh; ++k) {
     const int h = h0 + k;
     unsigned char* cur = smem + (k & 1) * K::BUF;
-    if (k + 1 < nh) load_x<P, Q, N>(smem + ((k + 1) & 1) * K::BUF, x, dA_cs, dt_T, b, c, h + 1, L, H, nc);
+    if (k + 1 < nh) load_x<P, Q, N>(sbase + ((k + 1) & 1) * K::BUF, x, dA_cs, dt_T, b, c, h + 1, L, H, nc);
     // Scale x rows by w_j in place (each 16-byte slot belongs to row s / 8).
     {
       const float* css = (const float*)(cur + K::XS_BYTES);
@@ -158,7 +153,7 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
         *p = o;
       }
     }
-    __syncthreads();
+    lds_barrier();  // scaled x visible; next head's loads stay in flight
     f32x4 acc[NTW][PT];
 #pragma unroll
     for (int a = 0; a < NTW; ++a)
@@ -190,7 +185,7 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) *(f32x4*)(row + 4 * nt) = acc[nt][pt];
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 

@@ -48,6 +48,39 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// 16-byte direct-to-LDS load (global_load_lds_dwordx4): lane l's 16 bytes from
+// `src` land at LDS byte address lds_base + 16 l; lds_base (an LDS byte
+// address, see lds_addr) must be uniform across the wave.  Issued through
+// inline asm so that the compiler does not see an LDS write it cannot
+// disambiguate from later LDS reads of the other buffer (it would then wait
+// for the load right away and undo the prefetch).  The caller owns the
+// ordering: the issuing waves wait vmcnt(0), then a barrier, before any wave
+// reads the destination.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const void* lds_ptr;
+  return (uint32_t)(uintptr_t)(lds_ptr)(p);
+}
+
+// Workgroup barrier that orders LDS traffic only: waits for this wave's LDS
+// operations (lgkmcnt 0), leaves its global loads, stores and direct-to-LDS
+// loads in flight, then meets the other waves.  __syncthreads() would also
+// wait for every outstanding global operation (vmcnt 0), which serialises a
+// prefetch issued just before it.  Data brought in by direct-to-LDS loads is
+// only safe to read after an explicit vmcnt wait by the issuing wave followed
+// by a barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt(63) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
