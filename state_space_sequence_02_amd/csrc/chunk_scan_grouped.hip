@@ -51,8 +51,12 @@ template <int RLH>
 __device__ __forceinline__ int hswz(int r, int c) {
   return c ^ (((r & 3) | (((r >> 4) & 3) << 2)) & (RLH - 1));
 }
-// Chunk position of 16-byte chunk c of x row r (8 chunks per row).
-__device__ __forceinline__ int xswz(int r, int c) { return c ^ (r & 7); }
+// Chunk position of 16-byte chunk c of x row r (8 chunks per row).  A
+// transpose read touches 16 rows 4g + e (+ 32 jp) and, per row, four chunks
+// of the same parity; xor-ing with (r >> 1) alternates that parity between
+// neighbouring even (and odd) rows so two rows share each bank group, the
+// least 16-byte chunks allow.
+__device__ __forceinline__ int xswz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // Issues the direct-to-LDS loads of one head into buffer `buf`:
 // state rows (P x N bf16), x rows (Q x P bf16, rows past L clamped to L-1,
@@ -99,65 +103,86 @@ __device__ __forceinline__ void load_head(uint32_t buf, const bf16* __restrict__
 }
 
 
-// Masked, decayed in-chunk contribution of one 16-row i-tile t (see the
-// per-head kernel): scales the carried-state part of Yt by 2^cs_i, then adds
-// sum over j-tiles 0..t of x^T (G^T * 2^(cs_i - cs_j) * dt_j, causal, + D on
-// the diagonal).  lws[j] = cs_j - log2(dt_j) folds dt_j into the exponent
-// (dt_j = 0 gives +inf and a zero weight), so a tile strictly below the
-// diagonal costs one subtract, one exp2 and one multiply per element; only
-// the diagonal tile is masked.  css/lws/Xs are this head's LDS tiles.
-template <int QT, bool REV, int P>
-__device__ __forceinline__ void finish_tile(const f32x4 (&Gs)[QT + 1], f32x4 (&Yt)[P / 16], int t,
-                                            const float* css, const float* lws,
-                                            const unsigned char* Xs, float Dh) {
+// Four elements (rows j = j0 + r) of the masked, decayed in-chunk weights of
+// column i: G^T * 2^(cs_i - cs_j) * dt_j, with lw_j = cs_j - log2(dt_j)
+// (dt_j = 0 gives +inf and weight 0).  Tiles strictly below the diagonal need
+// no mask; the diagonal tile is masked causally and carries the skip term D
+// on j == i, where the decay is 1.
+__device__ __forceinline__ void weights4(bf16x8& gm, int half, const f32x4 gt, const f32x4 lw,
+                                         float csi, bool diag, int j0, int i, float Dh) {
+  if (!diag) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) gm[half * 4 + r] = f2bf(gt[r] * fast_exp2(csi - lw[r]));
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + r;
+      float gv = (j <= i) ? gt[r] * fast_exp2(csi - lw[r]) : 0.f;
+      if (j == i) gv += Dh;
+      gm[half * 4 + r] = f2bf(gv);
+    }
+  }
+}
+
+// In-chunk contribution for both of a wave's i-tiles (t0 < t1): scales the
+// carried-state parts by 2^cs_i, then walks the j-tile pairs once, reading
+// each pair's x operand and weight exponents a single time and applying them
+// to every i-tile at or below the pair.  G^T tile (jt, t0) sits in slot jt,
+// (jt, t1) in slot QT - jt.
+template <int QT, int P>
+__device__ __forceinline__ void in_chunk(const f32x4 (&Gs)[QT + 1], f32x4 (&Y0)[P / 16],
+                                         f32x4 (&Y1)[P / 16], int t0, int t1, const float* css,
+                                         const float* lws, const unsigned char* Xs, float Dh) {
   constexpr int PT = P / 16;
   const int lane = lane_id();
   const int L16 = lane & 15, grp = lane >> 4;
-  const int i = 16 * t + L16;
-  const float csi = css[i];
-  const float sc = fast_exp2(csi);
+  const int i0 = 16 * t0 + L16, i1 = 16 * t1 + L16;
+  const float cs0 = css[i0], cs1 = css[i1];
+  const float sc0 = fast_exp2(cs0), sc1 = fast_exp2(cs1);
 #pragma unroll
-  for (int pt = 0; pt < PT; ++pt) Yt[pt] *= sc;
-  // j-tile jt of the wave's first i-tile sits in slot jt, of its second i-tile
-  // in slot QT - jt; NG bounds the j-tiles either can have.
-  constexpr int NG = REV ? QT : QT / 2;
+  for (int pt = 0; pt < PT; ++pt) {
+    Y0[pt] *= sc0;
+    Y1[pt] *= sc1;
+  }
 #pragma unroll
-  for (int jp = 0; jp < (NG + 1) / 2; ++jp) {
-    if (2 * jp > t) break;
-    bf16x8 gm;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int jt = 2 * jp + half;
-      const int slot = REV ? QT - (jt < NG ? jt : 0) : (jt < NG ? jt : 0);
-      if (jt < NG && jt < t) {
-        const f32x4 gt = Gs[slot];
-        const f32x4 lw = *(const f32x4*)(lws + 16 * jt + 4 * grp);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gm[half * 4 + r] = f2bf(gt[r] * fast_exp2(csi - lw[r]));
-      } else if (jt < NG && jt == t) {
-        const f32x4 gt = Gs[slot];
-        const f32x4 lw = *(const f32x4*)(lws + 16 * jt + 4 * grp);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * jt + 4 * grp + r;
-          float gv = (j <= i) ? gt[r] * fast_exp2(csi - lw[r]) : 0.f;
-          if (j == i) gv += Dh;
-          gm[half * 4 + r] = f2bf(gv);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gm[half * 4 + r] = f2bf(0.f);
-      }
-    }
+  for (int jp = 0; jp < QT / 2; ++jp) {
+    if (2 * jp > t1) break;
+    const int ja = 2 * jp, jb = 2 * jp + 1;
     const int ra = 32 * jp + 4 * grp + (L16 >> 2), rb = ra + 16;
+    bf16x8 xop[PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
       const int p0 = 4 * PT * (L16 & 3) + 4 * pt;
       const int ch = p0 >> 3, off = (p0 & 7) * 2;
       const bf16* pa = (const bf16*)(Xs + ra * (P * 2) + (xswz(ra, ch) << 4) + off);
       const bf16* pb = (const bf16*)(Xs + rb * (P * 2) + (xswz(rb, ch) << 4) + off);
-      const bf16x8 xop = cat(lds_read_tr(pa), lds_read_tr(pb));
-      Yt[pt] = mfma16x16x32(xop, gm, Yt[pt]);
+      xop[pt] = cat(lds_read_tr(pa), lds_read_tr(pb));
+    }
+    const f32x4 lwa = *(const f32x4*)(lws + 16 * ja + 4 * grp);
+    const f32x4 lwb = *(const f32x4*)(lws + 16 * jb + 4 * grp);
+    {  // tile t1 (2 jp <= t1 here)
+      bf16x8 gm;
+      weights4(gm, 0, Gs[QT - ja], lwa, cs1, ja == t1, 16 * ja + 4 * grp, i1, Dh);
+      if (jb <= t1) {
+        weights4(gm, 1, Gs[QT - jb], lwb, cs1, jb == t1, 16 * jb + 4 * grp, i1, Dh);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gm[4 + r] = f2bf(0.f);
+      }
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) Y1[pt] = mfma16x16x32(xop[pt], gm, Y1[pt]);
+    }
+    if (ja < QT / 2 && ja <= t0) {  // tile t0
+      bf16x8 gm;
+      weights4(gm, 0, Gs[ja < QT / 2 ? ja : 0], lwa, cs0, ja == t0, 16 * ja + 4 * grp, i0, Dh);
+      if (jb < QT / 2 && jb <= t0) {
+        weights4(gm, 1, Gs[jb < QT / 2 ? jb : 0], lwb, cs0, jb == t0, 16 * jb + 4 * grp, i0, Dh);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gm[4 + r] = f2bf(0.f);
+      }
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) Y0[pt] = mfma16x16x32(xop[pt], gm, Y0[pt]);
     }
   }
 }
@@ -300,8 +325,7 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
     }
     lds_barrier();  // weights visible; next head's loads stay in flight
     const float Dh = Dv ? Dv[h] : 0.f;
-    finish_tile<QT, false, P>(Gs, Y[0], t0, css, dts, Xs, Dh);
-    finish_tile<QT, true, P>(Gs, Y[1], t1, css, dts, Xs, Dh);
+    in_chunk<QT, P>(Gs, Y[0], Y[1], t0, t1, css, dts, Xs, Dh);
 
     __builtin_amdgcn_s_waitcnt(0);  // next head's bytes have landed (and older stores drained)
     const int64_t valid = L - tok0;
