@@ -38,7 +38,8 @@ def stage_model(w):
     """Algorithmic flops and HBM bytes per launch of each stage of the fused
     forward: every input read once and every output written once, in the
     dtypes that stage consumes and produces; flops count the causal triangle
-    (diagonal included) and nothing above it."""
+    (diagonal included) and nothing above it, and the C B^T products once per
+    (chunk, group), since every head of the group shares them."""
     B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
     nc = w.nchunks
     e = 4 if w.dtype == "f32" else 2
@@ -53,7 +54,8 @@ def stage_model(w):
     m["chunk_state"] = dict(flops=2 * N * P * tok * H, bytes=x + bc + 2 * csb + st)
     m["state_passing"] = dict(flops=2 * st // 4, bytes=st + hs + B * H * nc * 4 + fin)
     m["chunk_scan"] = dict(
-        flops=tok * H * (2 * N * P + (Q + 1) * N + (Q + 1) * P + 2 * P),
+        # C B^T depends only on the (chunk, group): counted once per group
+        flops=tok * H * (2 * N * P + (Q + 1) * P + 2 * P) + tok * G * (Q + 1) * N,
         bytes=x + 2 * bc + 2 * csb + hs + H * 4 + x)
     return m
 
