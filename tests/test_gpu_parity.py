@@ -203,20 +203,31 @@ def test_chunk_size_invariance(m2, Q):
 
 
 def test_split_sequence_resume(m2):
-    """Running [0, s) then [s, L) from the first part's final state matches one run."""
+    """Running [0, s) then [s, L) from the first part's final state matches one run.
+
+    On a chunk boundary (s = 512) both runs perform the same chunks, so the
+    final states agree to float32 accumulation order.  Off a boundary
+    (s = 700) the second part is chunked differently, so its weighted inputs
+    round to bfloat16 differently: both runs must meet the oracle at the
+    bfloat16 tolerance and differ from each other by no more than about one
+    bfloat16 rounding of the state's inputs (2^-8)."""
     w = _custom(name="split", batch=1, seqlen=1280, nheads=4, headdim=64, dstate=64, ngroups=1,
                 chunk_size=256, init_state=True, seed=34)
     inp = ssd_inputs.make_inputs(w)
     g = to_gpu(inp)
+    o = oracle_inputs(inp)
+    _, ofin, _ = oracle.ssd_recurrence(o["x"], o["dt"], o["A"], o["B"], o["C"], o["D"],
+                                       o["init_state"], chunk_size=256)
     y, fin = run_forward(m2, g, 256)
-    for s in (512, 700):
+    for s, tol in ((512, 1e-5), (700, 2.0 ** -8)):
         a = {k: (v[:, :s].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in g.items()}
         b = {k: (v[:, s:].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in g.items()}
         ya, fa = run_forward(m2, a, 256)
         b["init_state"] = fa
         yb, fb = run_forward(m2, b, 256)
         assert normwise(f64(torch.cat([ya, yb], 1)), f64(y)) <= 1e-2
-        assert normwise(f64(fb), f64(fin)) <= 1e-4
+        assert normwise(f64(fb), f64(fin)) <= tol, s
+        assert normwise(f64(fb), ofin) <= TOL["bf16"], s
 
 
 def test_bitwise_deterministic(m2):
