@@ -31,6 +31,11 @@ namespace m2 {
 
 namespace {
 
+#ifndef M2_HOP_AHEAD
+#define M2_HOP_AHEAD 3
+#endif
+constexpr int kHopAhead = M2_HOP_AHEAD;  // state-operand reads in flight ahead of the MFMAs
+
 template <int P, int Q, int N>
 struct GCfg {
   static constexpr int QT = Q / 16, NW = Q / 32, PT = P / 16, NBLK = N / 64;
@@ -305,19 +310,32 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
     f32x4 Y[2][PT];
 #pragma unroll
     for (int a = 0; a < PT; ++a) Y[0][a] = Y[1][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // carried-state term: Y^T[p, i] = sum_n h[p, n] C[i, n]
+    // carried-state term: Y^T[p, i] = sum_n h[p, n] C[i, n].  The state
+    // operands are read kHopAhead MFMA pairs ahead of use (a small register
+    // ring), so several LDS reads are in flight while the MFMAs run.
+    {
+      constexpr int NIT = NBLK * 2 * PT;
+      auto hop_at = [&](int it) {
+        const int nb = it / (2 * PT), kk = (it / PT) % 2, pt = it % PT;
+        const int r = 16 * (L16 >> 2) + 4 * pt + (L16 & 3);
+        const int cc = nb * 8 + kk * 4 + grp;
+        return *(const bf16x8*)(Hs + r * (N * 2) + (hswz<K::RLH>(r, cc) << 4));
+      };
+      bf16x8 ring[kHopAhead];
 #pragma unroll
-    for (int nb = 0; nb < NBLK; ++nb)
+      for (int a = 0; a < kHopAhead; ++a) ring[a] = hop_at(a);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          const int r = 16 * (L16 >> 2) + 4 * pt + (L16 & 3);
-          const int cc = nb * 8 + kk * 4 + grp;
-          const bf16x8 hop = *(const bf16x8*)(Hs + r * (N * 2) + (hswz<K::RLH>(r, cc) << 4));
-          Y[0][pt] = mfma16x16x32(hop, C0[nb][kk], Y[0][pt]);
-          Y[1][pt] = mfma16x16x32(hop, C1[nb][kk], Y[1][pt]);
-        }
+      for (int it = 0; it < NIT; ++it) {
+        const int nb = it / (2 * PT), kk = (it / PT) % 2, pt = it % PT;
+        const bf16x8 hop = ring[it % kHopAhead];
+        if (it + kHopAhead < NIT) ring[it % kHopAhead] = hop_at(it + kHopAhead);
+        Y[0][pt] = mfma16x16x32(hop, C0[nb][kk], Y[0][pt]);
+        Y[1][pt] = mfma16x16x32(hop, C1[nb][kk], Y[1][pt]);
+        // keep each read where it is: the scheduler would otherwise sink it
+        // next to its MFMAs to shorten live ranges, one read in flight
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     // dt_j -> cs_j - log2(dt_j), in place (the in-chunk weights' exponent offset)
     if (tid < Q) {
       float* lw = (float*)dts;
