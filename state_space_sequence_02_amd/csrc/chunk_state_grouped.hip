@@ -140,17 +140,24 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
       const float* css = (const float*)(cur + K::XS_BYTES);
       const float* dts = css + Q;
       const float cs_last = css[Q - 1];
+      // every read first, then every write: interleaved, each write would
+      // order the next read behind it (one LDS round trip per slot)
+      constexpr int NS = Q * 8 / K::NT;
+      bf16x8 v[NS];
+      float wr[NS];
 #pragma unroll
-      for (int i = 0; i < Q * 8 / K::NT; ++i) {
+      for (int i = 0; i < NS; ++i) {
         const int s = tid + K::NT * i;
         const int r = s >> 3;
-        const float wr = fast_exp2(cs_last - css[r]) * dts[r];
-        bf16x8* p = (bf16x8*)(cur + s * 16);
-        const bf16x8 v = *p;
+        v[i] = *(const bf16x8*)(cur + s * 16);
+        wr[i] = fast_exp2(cs_last - css[r]) * dts[r];
+      }
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
         bf16x8 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = f2bf(bf2f(v[e]) * wr);
-        *p = o;
+        for (int e = 0; e < 8; ++e) o[e] = f2bf(bf2f(v[i][e]) * wr[i]);
+        *(bf16x8*)(cur + (tid + K::NT * i) * 16) = o;
       }
     }
     lds_barrier();  // scaled x visible; next head's loads stay in flight
