@@ -71,9 +71,15 @@ def main():
                     help="tokens per head for the CPU oracle sample (0 = whole sequence)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--decode-batch", type=int, default=0,
+                    help="only measure the one-token recurrent step at this batch size "
+                         "(H=32, P=64, N=256, bf16)")
     args = ap.parse_args()
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.decode_batch:
+        decode_bench(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
@@ -215,6 +221,48 @@ def copy_probe(mib):
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
                       "launches": 5}), flush=True)
+
+
+def decode_bench(args):
+    """One-token recurrent step (mamba2_decode_step) on a serving-sized batch:
+    tokens/s = batch / step time, and the state's HBM roofline (the float32
+    state is read and written once per step; the per-token inputs are
+    negligible next to it)."""
+    import torch
+
+    import ssd_inputs
+    import state_space_sequence_02_amd as m2
+
+    w = ssd_inputs.custom(name=f"decode_B{args.decode_batch}_H32_P64_N256", batch=args.decode_batch,
+                          seqlen=1, nheads=32, headdim=64, dstate=256, ngroups=1, chunk_size=64,
+                          init_state=True, seed=48)
+    inp = ssd_inputs.make_inputs(w)
+    g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    x, dt, Bm, C = (g[k][:, 0].clone() for k in ("x", "dt", "B", "C"))
+    state = g["init_state"].clone()
+    y = torch.empty_like(x)
+    dims = m2.make_dims(w.batch, 1, w.nheads, w.headdim, w.dstate, 1, 64, torch.bfloat16)
+    for _ in range(args.warmup):
+        m2.mamba2_decode_step(dims, x, dt, g["A"], Bm, C, g["D"], state, y)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        m2.mamba2_decode_step(dims, x, dt, g["A"], Bm, C, g["D"], state, y)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    sbytes = 2 * state.numel() * 4
+    ibytes = (x.numel() + dt.numel() + Bm.numel() + C.numel() + y.numel()) * 2
+    gbs = (sbytes + ibytes) / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "SSD one-token decode step tokens/s (B sequences, H=32, P=64, N=256) on 1 MI355X",
+        "value": w.batch / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic", "config": {"workload": w.name, "batch": w.batch},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+    }), flush=True)
 
 
 def cpu_baseline(inp, w, tokens_per_head):

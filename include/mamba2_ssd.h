@@ -181,6 +181,28 @@ int mamba2_ssd_forward_profile(const mamba2_dims* dims, const void* x, const voi
                                void* workspace, size_t workspace_bytes, void* stream,
                                float* stage_ms);
 
+/*
+ * Recurrent single-token step: the constant-memory inference mode of the same
+ * recurrence (pages: devotd.net news item, section 1 - a fixed-size hidden
+ * state updated as tokens are processed; disconfirmai.com, abstract - the
+ * recurrent state).  For one new token of every (batch, head), in place:
+ *     state[b,h] = exp(dt[b,h] * A[h]) * state[b,h] + dt[b,h] * x[b,h] (outer) B[b,g]
+ *     y[b,h]     = state[b,h] . C[b,g] + D[h] * x[b,h]          (g = h / (H/G))
+ * i.e. one token of the forward pass, reading the state after the update.
+ * dims: seqlen must be 1 (MAMBA2_ERR_SHAPE otherwise); chunk_size is not
+ *       used but must be a supported value, as for every dims.
+ * Layouts: x, y [B, H, P] (the forward's [B, L, H, P] with L = 1);
+ *          dt [B, H]; B, C [B, G, N]; A, D [H] float32 (D may be NULL);
+ *          state [B, H, P, N] float32, read and overwritten.
+ * dtype as for the forward: bfloat16 makes x, dt, B, C and y bfloat16.
+ * Every pointer 16-byte aligned, as everywhere (a per-token view sliced out
+ * of a [B, L, ...] tensor usually is not: copy it).
+ * Bound by HBM on the state (read once, written once).
+ */
+int mamba2_decode_step(const mamba2_dims* dims, const void* x, const void* dt, const float* A,
+                       const void* B, const void* C, const float* D, float* state, void* y,
+                       void* stream);
+
 /* Static description of a status code. */
 const char* mamba2_status_string(int status);
 

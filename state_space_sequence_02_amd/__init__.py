@@ -39,7 +39,8 @@ MAMBA2_DTYPE_BF16 = 1
 EXPORTS = (
     "mamba2_validate", "mamba2_chunk_cumsum", "mamba2_chunk_state", "mamba2_state_passing",
     "mamba2_chunk_scan", "mamba2_ssd_workspace_bytes", "mamba2_ssd_forward",
-    "mamba2_ssd_forward_profile", "mamba2_status_string", "mamba2_last_error",
+    "mamba2_ssd_forward_profile", "mamba2_decode_step", "mamba2_status_string",
+    "mamba2_last_error",
 )
 
 
@@ -78,6 +79,7 @@ def _load():
         "mamba2_ssd_forward": ([D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P], ctypes.c_int),
         "mamba2_ssd_forward_profile": ([D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
                                         ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
+        "mamba2_decode_step": ([D, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "mamba2_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "mamba2_last_error": ([], ctypes.c_char_p),
     }
@@ -185,6 +187,23 @@ def mamba2_ssd_forward_profile(dims, x, dt, A, B, C, D, init_state, y, final_sta
                                            int(workspace_bytes), _stream(stream), ms),
            "mamba2_ssd_forward_profile")
     return [float(v) for v in ms]
+
+
+def mamba2_decode_step(dims, x, dt, A, B, C, D, state, y, stream=None):
+    _check(_lib.mamba2_decode_step(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                   _ptr(C), _ptr(D), _ptr(state), _ptr(y), _stream(stream)),
+           "mamba2_decode_step")
+
+
+def decode_step(x, dt, A, B, C, D, state, *, chunk_size=64, stream=None):
+    """One token per (batch, head): x[B,H,P], dt[B,H], B/C[B,G,N]; updates the
+    float32 state[B,H,P,N] in place and returns y[B,H,P] (allocated with torch)."""
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dims = make_dims(b, 1, H, P, N, G, chunk_size, x.dtype)
+    y = torch.empty_like(x)
+    mamba2_decode_step(dims, x, dt, A, B, C, D, state, y, stream)
+    return y
 
 
 def ssd_forward(x, dt, A, B, C, D=None, init_state=None, *, chunk_size=256, workspace=None,

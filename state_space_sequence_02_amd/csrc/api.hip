@@ -307,6 +307,26 @@ int mamba2_ssd_forward_profile(const mamba2_dims* dims, const void* x, const voi
   return rc;
 }
 
+int mamba2_decode_step(const mamba2_dims* dims, const void* x, const void* dt, const float* A,
+                       const void* B, const void* C, const float* D, float* state, void* y,
+                       void* stream) {
+  m2::Dims d;
+  CHECK(validate(dims, &d));
+  if (d.L != 1)
+    return fail(MAMBA2_ERR_SHAPE, "decode_step advances one token: seqlen must be 1 (got %lld)",
+                (long long)d.L);
+  CHECK(need(x, "x"));
+  CHECK(need(dt, "dt"));
+  CHECK(need(A, "A"));
+  CHECK(need(B, "B"));
+  CHECK(need(C, "C"));
+  CHECK(maybe(D, "D"));
+  CHECK(need(state, "state"));
+  CHECK(need(y, "y"));
+  return hip_status(m2::launch_decode_step(d, x, dt, A, B, C, D, state, y, (hipStream_t)stream),
+                    "decode_step launch");
+}
+
 const char* mamba2_status_string(int status) {
   switch (status) {
     case MAMBA2_OK: return "ok";

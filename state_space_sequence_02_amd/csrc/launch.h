@@ -37,4 +37,10 @@ hipError_t launch_chunk_scan_grouped(const Dims& d, const void* x, const void* B
                                      const float* dA_cs, const float* dt_T, const void* hst,
                                      const float* D, void* y, hipStream_t s);
 
+// One-token recurrent step, in place on the float32 state [B,H,P,N];
+// x, y [B,H,P], dt [B,H], B, C [B,G,N].
+hipError_t launch_decode_step(const Dims& d, const void* x, const void* dt, const float* A,
+                              const void* B, const void* C, const float* D, float* state,
+                              void* y, hipStream_t s);
+
 }  // namespace m2

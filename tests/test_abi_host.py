@@ -113,3 +113,18 @@ def test_null_and_misaligned_pointers_rejected_on_host():
     assert rc == m2.MAMBA2_ERR_WORKSPACE
     rc = lib.mamba2_chunk_state(None, ok, ok, ok, ok, ok, 0)
     assert rc == m2.MAMBA2_ERR_NULL
+
+
+def test_decode_step_checks_on_host():
+    lib = m2._lib
+    ok = 1 << 20
+    d = _dims(seqlen=2)
+    rc = lib.mamba2_decode_step(ctypes.byref(d), ok, ok, ok, ok, ok, None, ok, ok, 0)
+    assert rc == m2.MAMBA2_ERR_SHAPE and "seqlen" in m2.mamba2_last_error()
+    d1 = _dims(seqlen=1)
+    rc = lib.mamba2_decode_step(ctypes.byref(d1), None, ok, ok, ok, ok, None, ok, ok, 0)
+    assert rc == m2.MAMBA2_ERR_NULL and "x" in m2.mamba2_last_error()
+    rc = lib.mamba2_decode_step(ctypes.byref(d1), ok, ok, ok, ok, ok, None, ok + 8, ok, 0)
+    assert rc == m2.MAMBA2_ERR_ALIGN and "state" in m2.mamba2_last_error()
+    rc = lib.mamba2_decode_step(ctypes.byref(d1), ok, ok, ok, ok, ok, ok + 4, ok, ok, 0)
+    assert rc == m2.MAMBA2_ERR_ALIGN and "D" in m2.mamba2_last_error()
