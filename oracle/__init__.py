@@ -55,9 +55,10 @@ def _load():
         lib.oracle_state_passing.argtypes = [ctypes.c_int64] * 5 + [P, P, P, P, P]
         lib.oracle_chunk_outputs.argtypes = [ctypes.POINTER(_Dims), P, P, P, P, P, P,
                                              ctypes.c_int, P, P, P]
+        lib.oracle_ssd_backward.argtypes = [ctypes.POINTER(_Dims)] + [P] * 16
         lib.oracle_num_threads.restype = ctypes.c_int
         for f in ("oracle_chunk_cumsum", "oracle_ssd_recurrence", "oracle_chunk_local_states",
-                  "oracle_state_passing", "oracle_chunk_outputs"):
+                  "oracle_state_passing", "oracle_chunk_outputs", "oracle_ssd_backward"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -165,3 +166,31 @@ def chunk_outputs(x, dt, A, B, C, D, h_start, *, chunk_size, heads=None):
                                         _ptr(C), _ptr(D), nsel, _ptr(hsel), _ptr(h_start),
                                         _ptr(y)), "oracle_chunk_outputs")
     return y
+
+
+def ssd_backward(x, dt, A, B, C, D, h0, dy, dfinal=None, *, chunk_size=64):
+    """Gradients of sum(dy * y) + sum(dfinal * final) with respect to every
+    input of ssd_recurrence, by back-propagation through the recurrence.
+    Returns a dict of float64 arrays: dx, ddt, dA, dB, dC (group gradients,
+    the heads of each group summed), dD (None when D is None) and dh0 (None
+    when h0 is None)."""
+    x, dt, A, B, C, D, h0, dy, dfinal = map(_f32, (x, dt, A, B, C, D, h0, dy, dfinal))
+    d = _dims(x, B, chunk_size)
+    Bn, L, H, P, N, G = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.ngroups
+    assert dy.shape == x.shape
+    dx = np.empty((Bn, L, H, P), np.float64)
+    ddt = np.empty((Bn, L, H), np.float64)
+    dBh = np.empty((Bn, L, H, N), np.float64)
+    dCh = np.empty((Bn, L, H, N), np.float64)
+    dA_part = np.empty((Bn, H), np.float64)
+    dD_part = np.empty((Bn, H), np.float64)
+    dh0 = np.empty((Bn, H, P, N), np.float64) if h0 is not None else None
+    _check(_load().oracle_ssd_backward(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                       _ptr(C), _ptr(D), _ptr(h0), _ptr(dy), _ptr(dfinal),
+                                       _ptr(dx), _ptr(ddt), _ptr(dBh), _ptr(dCh), _ptr(dA_part),
+                                       _ptr(dD_part), _ptr(dh0)), "oracle_ssd_backward")
+    hpg = H // G
+    return {"dx": dx, "ddt": ddt, "dA": dA_part.sum(0),
+            "dB": dBh.reshape(Bn, L, G, hpg, N).sum(3),
+            "dC": dCh.reshape(Bn, L, G, hpg, N).sum(3),
+            "dD": dD_part.sum(0) if D is not None else None, "dh0": dh0}

@@ -38,6 +38,8 @@
  *                               independent chunked form)
  *   oracle_state_passing        pinned (reproduces recurrence snapshots)
  *   oracle_chunk_outputs        pinned (reproduces recurrence outputs)
+ *   oracle_ssd_backward         pinned (central finite differences of
+ *                               oracle_ssd_recurrence, every input)
  * The head-to-group convention g = h / (H/G) is a stated convention: parity
  * unpinned against the pages, which do not fix it.
  *
@@ -315,4 +317,115 @@ int oracle_chunk_outputs(const oracle_dims* d, const float* x, const float* dt,
     free(s);
   }
   return 0;
+}
+
+/*
+ * Gradients of the forward pass, by back-propagation through the same
+ * token-by-token recurrence (reverse-mode differentiation of the definition
+ * above).  The pages give no backward pass; the disconfirmai.com summary
+ * ("Jane Street ML Engineers Map Mamba-2 Recurrent State Computation to
+ * Tensor Cores with cuTile", lead paragraph) notes that the forward speedups
+ * rest on a backward implementation that is not yet published.  For the scalar
+ *     loss = sum_{t,p} dy[b,t,h,p] y[b,t,h,p] + sum dfinal[b,h] . s_L
+ * with s_{t+1} = a_t s_t + dt_t x_t (outer) B_t (s_0 = h0) and
+ * y_t = s_{t+1} . C_t + D x_t, a row p of the state walks time backwards
+ * with g = d loss / d s_{t+1}:
+ *     g          = dfinal row, then at each t (descending): g += dy_t[p] C_t
+ *     dC_t      += dy_t[p] s_{t+1}         dx_t[p]  = D dy_t[p] + dt_t (g . B_t)
+ *     dB_t      += dt_t x_t[p] g           ddt_t   += x_t[p] (g . B_t) + A a_t (g . s_t)
+ *     dA        += dt_t a_t (g . s_t)      dD      += dy_t[p] x_t[p]
+ *     g          = a_t g                   (after t = 0: dh0 row = g)
+ * Outputs (double): dx[B,L,H,P], ddt[B,L,H], per-head parts of the group
+ * gradients dBh, dCh[B,L,H,N] (the caller sums the heads of each group),
+ * per-(batch, head) parts dA_part, dD_part[B,H], and dh0[B,H,P,N] (nullable).
+ * dy[B,L,H,P] is required; dfinal[B,H,P,N], D and h0 may be NULL.
+ * Each (b, h) runs in one thread, its rows in order, so every output element
+ * has a single writer.
+ */
+int oracle_ssd_backward(const oracle_dims* d, const float* x, const float* dt,
+                        const float* A, const float* Bm, const float* C, const float* D,
+                        const float* h0, const float* dy, const float* dfinal, double* dx,
+                        double* ddt, double* dBh, double* dCh, double* dA_part,
+                        double* dD_part, double* dh0) {
+  if (!dims_ok(d)) return 1;
+  if (!x || !dt || !A || !Bm || !C || !dy || !dx || !ddt || !dBh || !dCh || !dA_part ||
+      !dD_part)
+    return 1;
+  const int64_t Bn = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim;
+  const int64_t N = d->dstate, G = d->ngroups, hpg = H / G;
+  const int64_t units = Bn * H;
+  int rc = 0;
+#pragma omp parallel
+  {
+    /* states s_0 .. s_L of one row, and the running adjoint */
+    double* s = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N));
+    double* g = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!s || !g) {
+#pragma omp atomic write
+      rc = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+      if (!s || !g) continue;
+      const int64_t b = u / H, h = u % H, gr = h / hpg;
+      const double Ah = (double)A[h], Dh = D ? (double)D[h] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        ddt[(b * L + t) * H + h] = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          dBh[((b * L + t) * H + h) * N + n] = 0.0;
+          dCh[((b * L + t) * H + h) * N + n] = 0.0;
+        }
+      }
+      double dA_acc = 0.0, dD_acc = 0.0;
+      for (int64_t p = 0; p < P; ++p) {
+        for (int64_t n = 0; n < N; ++n)
+          s[n] = h0 ? (double)h0[((b * H + h) * P + p) * N + n] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+          const double dtv = (double)dt[(b * L + t) * H + h];
+          const double a = exp(dtv * Ah);
+          const double xv = (double)x[((b * L + t) * H + h) * P + p];
+          const float* Bt = Bm + ((b * L + t) * G + gr) * N;
+          const double* sp = s + t * N;
+          double* sn = s + (t + 1) * N;
+          for (int64_t n = 0; n < N; ++n) sn[n] = a * sp[n] + dtv * xv * (double)Bt[n];
+        }
+        for (int64_t n = 0; n < N; ++n)
+          g[n] = dfinal ? (double)dfinal[((b * H + h) * P + p) * N + n] : 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+          const double dtv = (double)dt[(b * L + t) * H + h];
+          const double a = exp(dtv * Ah);
+          const double xv = (double)x[((b * L + t) * H + h) * P + p];
+          const double dyv = (double)dy[((b * L + t) * H + h) * P + p];
+          const float* Bt = Bm + ((b * L + t) * G + gr) * N;
+          const float* Ct = C + ((b * L + t) * G + gr) * N;
+          const double* sp = s + t * N;
+          const double* sn = s + (t + 1) * N;
+          double* dBt = dBh + ((b * L + t) * H + h) * N;
+          double* dCt = dCh + ((b * L + t) * H + h) * N;
+          double gB = 0.0, gs = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            g[n] += dyv * (double)Ct[n];
+            dCt[n] += dyv * sn[n];
+            dBt[n] += dtv * xv * g[n];
+            gB += g[n] * (double)Bt[n];
+            gs += g[n] * sp[n];
+          }
+          dx[((b * L + t) * H + h) * P + p] = Dh * dyv + dtv * gB;
+          ddt[(b * L + t) * H + h] += xv * gB + Ah * a * gs;
+          dA_acc += dtv * a * gs;
+          dD_acc += dyv * xv;
+          for (int64_t n = 0; n < N; ++n) g[n] *= a;
+        }
+        if (dh0) {
+          double* o = dh0 + ((b * H + h) * P + p) * N;
+          for (int64_t n = 0; n < N; ++n) o[n] = g[n];
+        }
+      }
+      dA_part[b * H + h] = dA_acc;
+      dD_part[b * H + h] = dD_acc;
+    }
+    free(s);
+    free(g);
+  }
+  return rc;
 }
