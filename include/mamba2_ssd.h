@@ -203,6 +203,50 @@ int mamba2_decode_step(const mamba2_dims* dims, const void* x, const void* dt, c
                        const void* B, const void* C, const float* D, float* state, void* y,
                        void* stream);
 
+/*
+ * Backward pass: gradients of a scalar loss through mamba2_ssd_forward.  The
+ * pages publish no backward pass (disconfirmai.com, lead paragraph: the
+ * forward speedups rest on one that is not yet published); this is the exact
+ * derivative of the forward's chunked form (devotd.net news item, section 2),
+ * for the loss whose gradients with respect to y and final_state are dy and
+ * dfinal:
+ *     dx, ddt, dB, dC   same layouts and dtype as x, dt, B, C
+ *     dA [H], dD [H]    float32 (dD written only when D is non-NULL; it is
+ *                       required then)
+ *     dinit [B,H,P,N]   float32, may be NULL (not written); it is the
+ *                       gradient with respect to init_state (whether or not
+ *                       init_state is NULL, which means a zero start)
+ * Inputs are the forward's (x, dt, A, B, C, D, init_state; D and init_state
+ * may be NULL), dy [B,L,H,P] (dtype of dims) and dfinal [B,H,P,N] float32
+ * (NULL = zero).  The forward quantities the gradients need are recomputed
+ * inside (nothing from an earlier forward call is read).
+ * Supported: bfloat16 with headdim 64, dstate 64, 128 or 256 and chunk_size
+ * 64, 128 or 256 (MAMBA2_ERR_UNSUPPORTED otherwise).  Workspace: at least
+ * mamba2_ssd_backward_workspace_bytes(dims), 256-byte aligned, contents on
+ * return unspecified.  Pointer, stream and error rules as for the forward.
+ */
+size_t mamba2_ssd_backward_workspace_bytes(const mamba2_dims* dims);
+
+int mamba2_ssd_backward(const mamba2_dims* dims, const void* x, const void* dt, const float* A,
+                        const void* B, const void* C, const float* D, const float* init_state,
+                        const void* dy, const float* dfinal, void* dx, void* ddt, float* dA,
+                        void* dB, void* dC, float* dD, float* dinit, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Same as mamba2_ssd_backward, then waits and writes the device time of each
+ * of its eight stages in milliseconds to stage_ms[0..7]: chunk_cumsum,
+ * chunk_state, state_passing (the recomputed forward states), adjoint
+ * chunk_state, reverse state_passing, dB/dC kernel, dx kernel, dA/dD sums.
+ * For measurement only (creates events, blocks).
+ */
+int mamba2_ssd_backward_profile(const mamba2_dims* dims, const void* x, const void* dt,
+                                const float* A, const void* B, const void* C, const float* D,
+                                const float* init_state, const void* dy, const float* dfinal,
+                                void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD,
+                                float* dinit, void* workspace, size_t workspace_bytes,
+                                void* stream, float* stage_ms);
+
 /* Static description of a status code. */
 const char* mamba2_status_string(int status);
 

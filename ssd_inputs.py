@@ -110,3 +110,17 @@ def make_inputs(w: Workload) -> dict:
     if w.init_state:
         h0 = 0.1 * torch.randn((Bn, H, P, N), generator=g, dtype=torch.float32)
     return {"x": x, "dt": dt, "A": A.contiguous(), "B": B, "C": C, "D": D, "init_state": h0}
+
+
+def make_cotangents(w: Workload) -> dict:
+    """Seeded upstream gradients for the backward pass: ``dy[B,L,H,P]`` in the
+    workload's dtype and ``dfinal[B,H,P,N]`` float32, both standard normal
+    (their own stream, seed + 1000003, so the forward inputs are unchanged)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed + 1000003)
+    io = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    dy = torch.randn((w.batch, w.seqlen, w.nheads, w.headdim), generator=g,
+                     dtype=torch.float32).to(io)
+    dfinal = torch.randn((w.batch, w.nheads, w.headdim, w.dstate), generator=g,
+                         dtype=torch.float32)
+    return {"dy": dy, "dfinal": dfinal}

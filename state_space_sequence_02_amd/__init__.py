@@ -39,7 +39,8 @@ MAMBA2_DTYPE_BF16 = 1
 EXPORTS = (
     "mamba2_validate", "mamba2_chunk_cumsum", "mamba2_chunk_state", "mamba2_state_passing",
     "mamba2_chunk_scan", "mamba2_ssd_workspace_bytes", "mamba2_ssd_forward",
-    "mamba2_ssd_forward_profile", "mamba2_decode_step", "mamba2_status_string",
+    "mamba2_ssd_forward_profile", "mamba2_decode_step", "mamba2_ssd_backward_workspace_bytes",
+    "mamba2_ssd_backward", "mamba2_ssd_backward_profile", "mamba2_status_string",
     "mamba2_last_error",
 )
 
@@ -80,6 +81,9 @@ def _load():
         "mamba2_ssd_forward_profile": ([D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
                                         ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
         "mamba2_decode_step": ([D, P, P, P, P, P, P, P, P, P], ctypes.c_int),
+        "mamba2_ssd_backward_workspace_bytes": ([D], ctypes.c_size_t),
+        "mamba2_ssd_backward": ([D] + [P] * 17 + [ctypes.c_size_t, P], ctypes.c_int),
+        "mamba2_ssd_backward_profile": ([D] + [P] * 17 + [ctypes.c_size_t, P, P], ctypes.c_int),
         "mamba2_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "mamba2_last_error": ([], ctypes.c_char_p),
     }
@@ -222,6 +226,61 @@ def ssd_forward(x, dt, A, B, C, D=None, init_state=None, *, chunk_size=256, work
     mamba2_ssd_forward(dims, x, dt, A, B, C, D, init_state, y, final, workspace,
                        workspace.numel() * workspace.element_size(), stream)
     return y, final
+
+
+def mamba2_ssd_backward_workspace_bytes(dims) -> int:
+    return int(_lib.mamba2_ssd_backward_workspace_bytes(ctypes.byref(dims)))
+
+
+def _bwd_args(dims, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB, dC, dD, dinit,
+              workspace, workspace_bytes):
+    return (ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(init_state), _ptr(dy), _ptr(dfinal), _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB),
+            _ptr(dC), _ptr(dD), _ptr(dinit), _ptr(workspace), int(workspace_bytes))
+
+
+def mamba2_ssd_backward(dims, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB, dC,
+                        dD, dinit, workspace, workspace_bytes, stream=None):
+    _check(_lib.mamba2_ssd_backward(*_bwd_args(dims, x, dt, A, B, C, D, init_state, dy, dfinal,
+                                               dx, ddt, dA, dB, dC, dD, dinit, workspace,
+                                               workspace_bytes), _stream(stream)),
+           "mamba2_ssd_backward")
+
+
+def mamba2_ssd_backward_profile(dims, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA,
+                                dB, dC, dD, dinit, workspace, workspace_bytes, stream=None):
+    """Runs mamba2_ssd_backward, waits, and returns its eight stage durations in ms."""
+    ms = (ctypes.c_float * 8)()
+    _check(_lib.mamba2_ssd_backward_profile(*_bwd_args(dims, x, dt, A, B, C, D, init_state, dy,
+                                                       dfinal, dx, ddt, dA, dB, dC, dD, dinit,
+                                                       workspace, workspace_bytes),
+                                            _stream(stream), ms),
+           "mamba2_ssd_backward_profile")
+    return [float(v) for v in ms]
+
+
+def ssd_backward(x, dt, A, B, C, D, init_state, dy, dfinal=None, *, chunk_size=256,
+                 workspace=None, stream=None):
+    """Allocates the gradients (and, unless given, the workspace) with torch on x's
+    device, runs mamba2_ssd_backward, and returns a dict with dx, ddt, dA, dB, dC,
+    dD (None without D) and dinit."""
+    dims = dims_of(x, B, chunk_size)
+    need = mamba2_ssd_backward_workspace_bytes(dims)
+    if need == 0:
+        _check(mamba2_validate(dims), "ssd_backward")
+        raise Mamba2Error(MAMBA2_ERR_UNSUPPORTED, "ssd_backward")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    dev = x.device
+    g = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt),
+         "dA": torch.empty_like(A), "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+         "dD": torch.empty_like(D) if D is not None else None,
+         "dinit": torch.empty((x.shape[0], x.shape[2], x.shape[3], B.shape[3]),
+                              dtype=torch.float32, device=dev)}
+    mamba2_ssd_backward(dims, x, dt, A, B, C, D, init_state, dy, dfinal, g["dx"], g["ddt"],
+                        g["dA"], g["dB"], g["dC"], g["dD"], g["dinit"], workspace,
+                        workspace.numel() * workspace.element_size(), stream)
+    return g
 
 
 def stage_buffers(dims, device):

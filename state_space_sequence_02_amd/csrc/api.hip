@@ -196,9 +196,182 @@ int check_forward_args(const mamba2_dims* dims, m2::Dims* d, const void* x, cons
   return MAMBA2_OK;
 }
 
+// Workspace of the backward pass: the forward quantities it recomputes
+// (dA_cs, dt_T, per-chunk states reused for the adjoint states, bf16 start
+// states, final state) and its own (bf16 end-of-chunk gradients, carried-state
+// and boundary dot-product parts, the groups' summed interaction matrices,
+// per-chunk dA and dD parts).
+struct BwdWorkspace {
+  size_t cs, st, hst, fin, th, wsum, dots, part, total;
+  int64_t wph;
+};
+
+BwdWorkspace plan_backward(const m2::Dims& d) {
+  BwdWorkspace w;
+  w.wph = m2::state_reverse_waves_per_head(d);
+  w.cs = round256((size_t)(d.B * d.H * d.nc * d.Q) * sizeof(float));
+  w.st = round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * sizeof(float));
+  w.hst = round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * 2);
+  w.fin = round256((size_t)(d.B * d.H * d.P * d.N) * sizeof(float));
+  w.th = round256((size_t)(d.B * d.nc * d.H * (d.N / 64) * d.Q) * sizeof(float));
+  w.wsum = round256((size_t)(d.B * d.nc * d.G) * (size_t)(d.Q * (d.Q + 16) / 2) * 2);
+  w.dots = round256((size_t)(d.B * d.H * d.nc * w.wph) * sizeof(float));
+  w.part = round256((size_t)(d.B * d.nc * d.H) * sizeof(float));
+  w.total = 2 * w.cs + w.st + 2 * w.hst + w.fin + w.th + w.wsum + w.dots + 2 * w.part;
+  return w;
+}
+
+constexpr int kBwdStages = 8;
+
+int enqueue_backward(const m2::Dims& d, const void* x, const void* dt, const float* A,
+                     const void* B, const void* C, const float* D, const float* init_state,
+                     const void* dy, const float* dfinal, void* dx, void* ddt, float* dA,
+                     void* dB, void* dC, float* dD, float* dinit, void* workspace,
+                     hipStream_t s, hipEvent_t* ev) {
+  const BwdWorkspace w = plan_backward(d);
+  char* p = (char*)workspace;
+  float* dA_cs = (float*)p;
+  p += w.cs;
+  float* dt_T = (float*)p;
+  p += w.cs;
+  float* st = (float*)p;
+  p += w.st;
+  void* hst = p;
+  p += w.hst;
+  void* gst = p;
+  p += w.hst;
+  float* fin = (float*)p;
+  p += w.fin;
+  float* th = (float*)p;
+  p += w.th;
+  void* wsum = p;
+  p += w.wsum;
+  float* dots = (float*)p;
+  p += w.dots;
+  float* dA_part = (float*)p;
+  p += w.part;
+  float* dD_part = (float*)p;
+  hipError_t e = hipSuccess;
+  int stage = 0;
+  auto mark = [&]() {
+    if (ev && e == hipSuccess) e = hipEventRecord(ev[stage], s);
+    ++stage;
+  };
+  mark();
+  e = e == hipSuccess ? m2::launch_chunk_cumsum(d, dt, A, dA_cs, dt_T, s) : e;
+  mark();
+  e = e == hipSuccess ? m2::launch_chunk_state_grouped(d, x, B, dA_cs, dt_T, st, s) : e;
+  mark();
+  e = e == hipSuccess ? m2::launch_state_passing_bf16(d, st, dA_cs, init_state, hst, fin, s) : e;
+  mark();
+  e = e == hipSuccess ? m2::launch_chunk_state_adjoint(d, dy, C, dA_cs, dt_T, st, s) : e;
+  mark();
+  e = e == hipSuccess
+          ? m2::launch_state_passing_reverse(d, st, dA_cs, dfinal, hst, gst, dinit, dots, s)
+          : e;
+  mark();
+  e = e == hipSuccess
+          ? m2::launch_chunk_bwd_dbdc(d, x, dy, B, C, dA_cs, dt_T, hst, gst, wsum, dB, dC, th, s)
+          : e;
+  mark();
+  e = e == hipSuccess ? m2::launch_chunk_bwd_dx(d, x, dy, B, C, dA_cs, dt_T, gst, dots,
+                                                (int)w.wph, th, A, D, dx, ddt, dA_part, dD_part, s)
+                      : e;
+  mark();
+  e = e == hipSuccess ? m2::launch_bwd_param_sums(d, dA_part, dD_part, dA, D ? dD : nullptr, s)
+                      : e;
+  mark();
+  return hip_status(e, "backward launch");
+}
+
+int check_backward_args(const mamba2_dims* dims, m2::Dims* d, const void* x, const void* dt,
+                        const float* A, const void* B, const void* C, const float* D,
+                        const float* init_state, const void* dy, const float* dfinal,
+                        void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD,
+                        float* dinit, void* workspace, size_t workspace_bytes) {
+  CHECK(validate(dims, d));
+  if (!m2::backward_supported(*d))
+    return fail(MAMBA2_ERR_UNSUPPORTED,
+                "backward needs bfloat16, headdim 64, dstate 64/128/256 and chunk_size "
+                "64/128/256");
+  CHECK(need(x, "x"));
+  CHECK(need(dt, "dt"));
+  CHECK(need(A, "A"));
+  CHECK(need(B, "B"));
+  CHECK(need(C, "C"));
+  CHECK(maybe(D, "D"));
+  CHECK(maybe(init_state, "init_state"));
+  CHECK(need(dy, "dy"));
+  CHECK(maybe(dfinal, "dfinal"));
+  CHECK(need(dx, "dx"));
+  CHECK(need(ddt, "ddt"));
+  CHECK(need(dA, "dA"));
+  CHECK(need(dB, "dB"));
+  CHECK(need(dC, "dC"));
+  if (D) CHECK(need(dD, "dD"));
+  CHECK(maybe(dinit, "dinit"));
+  const BwdWorkspace w = plan_backward(*d);
+  if (w.wph > 64)  // the dx kernel sums the boundary parts with one wavefront
+    return fail(MAMBA2_ERR_UNSUPPORTED, "state too large for the backward pass");
+  if (!workspace) return fail(MAMBA2_ERR_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(MAMBA2_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < w.total)
+    return fail(MAMBA2_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                w.total);
+  return MAMBA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t mamba2_ssd_backward_workspace_bytes(const mamba2_dims* dims) {
+  m2::Dims d;
+  if (validate(dims, &d) != MAMBA2_OK || !m2::backward_supported(d)) return 0;
+  return plan_backward(d).total;
+}
+
+int mamba2_ssd_backward(const mamba2_dims* dims, const void* x, const void* dt, const float* A,
+                        const void* B, const void* C, const float* D, const float* init_state,
+                        const void* dy, const float* dfinal, void* dx, void* ddt, float* dA,
+                        void* dB, void* dC, float* dD, float* dinit, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  m2::Dims d;
+  CHECK(check_backward_args(dims, &d, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB,
+                            dC, dD, dinit, workspace, workspace_bytes));
+  return enqueue_backward(d, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB, dC, dD,
+                          dinit, workspace, (hipStream_t)stream, nullptr);
+}
+
+int mamba2_ssd_backward_profile(const mamba2_dims* dims, const void* x, const void* dt,
+                                const float* A, const void* B, const void* C, const float* D,
+                                const float* init_state, const void* dy, const float* dfinal,
+                                void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD,
+                                float* dinit, void* workspace, size_t workspace_bytes,
+                                void* stream, float* stage_ms) {
+  m2::Dims d;
+  CHECK(check_backward_args(dims, &d, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB,
+                            dC, dD, dinit, workspace, workspace_bytes));
+  if (!stage_ms) return fail(MAMBA2_ERR_NULL, "stage_ms is NULL");
+  hipEvent_t ev[kBwdStages + 1] = {};
+  hipError_t e = hipSuccess;
+  for (int i = 0; i <= kBwdStages && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+  int rc = (e == hipSuccess) ? MAMBA2_OK : hip_status(e, "event create");
+  if (rc == MAMBA2_OK)
+    rc = enqueue_backward(d, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB, dC, dD,
+                          dinit, workspace, (hipStream_t)stream, ev);
+  if (rc == MAMBA2_OK) {
+    e = hipEventSynchronize(ev[kBwdStages]);
+    for (int i = 0; i < kBwdStages && e == hipSuccess; ++i)
+      e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+    rc = hip_status(e, "event timing");
+  }
+  for (int i = 0; i <= kBwdStages; ++i)
+    if (ev[i]) (void)hipEventDestroy(ev[i]);
+  return rc;
+}
+
 
 int mamba2_validate(const mamba2_dims* dims) {
   CHECK(validate(dims, nullptr));

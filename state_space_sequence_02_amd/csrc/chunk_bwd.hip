@@ -1,0 +1,841 @@
+// Backward pass of the chunked SSD: the in-chunk gradient kernels.  The pages
+// give only the forward pass and note that a backward pass is still to be
+// published (disconfirmai.com "Jane Street ML Engineers Map Mamba-2 Recurrent
+// State Computation to Tensor Cores with cuTile", lead paragraph); what is
+// computed here is the exact derivative of the forward's chunked form
+// (devotd.net news item on the Mamba-2 CUDA Tile forward-pass kernels,
+// section 2) written as matrix products.
+//
+// Per (batch, chunk, head), with cs the in-chunk cumulative log decay,
+// M[i, j] = 2^(cs_i - cs_j) for i >= j (else 0), CB = C B^T of the head's
+// group, dY and X the chunk's rows, h the chunk's start state, g the gradient
+// reaching its end state (both [P, N]) and y~ the forward output without the
+// D skip:
+//     dU  = (M o CB)^T dY + diag(2^(cs_last - cs)) B g^T         [Q, P]
+//     dx  = dt o dU + D dY
+//     dC += (M o W) B + diag(2^cs) dY h,   W = dY (dt o X)^T       (summed over
+//     dB += (M o W)^T C + diag(2^(cs_last - cs) dt) X g^T           the group's heads)
+//     d(A dt)_k = sum_{i >= k > j} T_ij + sum_{i >= k} T^h_i + sum_{j < k} T^S_j
+//                 + 2^cs_last <g, h>
+//     ddt_k = x_k . dU_k + A d(A dt)_k,   dA = sum_k dt_k d(A dt)_k,  dD = sum dy . x
+// with T_ij = (M o CB)_ij dt_j (dy_i . x_j) for i > j, T^h_i = 2^cs_i
+// dy_i . (h C_i) and T^S_j = dt_j x_j . dU^state_j: each sum collects terms
+// of single interactions whose decay spans position k, the form that does not
+// cancel (the equivalent suffix sum of dy . y~ - dt x . dU subtracts nearly
+// equal totals and loses the result to rounding).  <g, h> comes from the
+// reverse state pass, T^h from chunk_bwd_dbdc.
+//
+// Two kernels share the work.  chunk_bwd_dx: one workgroup per (batch, chunk,
+// group, run of heads); C B^T of the group is formed once and kept in float32
+// accumulators; per head the masked, decayed tiles go to LDS as bfloat16 and
+// feed dU^T = dY^T (M o CB) + ...; the epilogue forms dx, the row dot
+// products, the rectangle sums of T, ddt and the per-chunk parts of dA, dD.
+// chunk_bwd_wsum: one workgroup per (batch, chunk, group); per head W is
+// formed, masked and accumulated over the group's heads in float32 registers
+// (the group sum is taken before the products with B and C, so those run
+// once per group rather than once per head).  chunk_bwd_dbdc: one workgroup
+// per (batch, chunk, group, 64 state columns); per head the state terms (and
+// their T^h parts) accumulate in registers; the products of the summed W with
+// B and C follow once, from LDS.
+//
+// Both use 16x16x32 bfloat16 MFMA.  chunk_bwd_dx runs Q/32 waves; wave w owns
+// the output column tiles w and Q/16-1-w (equal causal work per wave) and the
+// lower-triangle tiles of the Q x Q interaction matrix in the row strips of
+// those two tiles (Q/16 + 1).
+#include "common.h"
+#include "launch.h"
+
+namespace m2 {
+
+namespace {
+
+template <int Q>
+struct BwdCfg {
+  static constexpr int P = 64, QT = Q / 16, NW = Q / 32, NT = 64 * NW;
+  static constexpr int NTILE = QT * (QT + 1) / 2;  // lower-triangle 16x16 tiles
+  static constexpr int SLOTS = QT + 1;             // of them per wave
+  static_assert(NTILE == NW * SLOTS, "triangle tiles split evenly over the waves");
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// The value, hidden from the optimiser: addresses computed from it inside a
+// loop stay inside the loop instead of being hoisted out of it and held in
+// registers for its whole length.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Triangle tile (ti >= tj) -> its index in the packed tile array.
+__device__ __forceinline__ int tix_of(int ti, int tj) { return ti * (ti + 1) / 2 + tj; }
+
+// Slot k of wave w: the row strips of tiles w and QT-1-w, (w, 0..w) then
+// (QT-1-w, 0..QT-1-w): QT+1 tiles for every wave.
+template <int QT>
+__device__ __forceinline__ int slot_ti(int w, int k) { return k <= w ? w : QT - 1 - w; }
+template <int QT>
+__device__ __forceinline__ int slot_tj(int w, int k) { return k <= w ? k : k - w - 1; }
+
+// rows [Q][64] of bfloat16 into LDS; row r comes from src + r * stride (in
+// elements), rows at or past `valid` are zero.
+template <int ROWS, int NT>
+__device__ __forceinline__ void load_rows64(bf16* dst, const bf16* __restrict__ src,
+                                            int64_t stride, int64_t valid) {
+  for (int s = threadIdx.x; s < ROWS * 8; s += NT) {
+    const int r = s >> 3, ch = s & 7;
+    bf16x8 v = zero8();
+    if (r < valid) v = *(const bf16x8*)(src + (int64_t)r * stride + ch * 8);
+    *(bf16x8*)(dst + r * 64 + ch * 8) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// chunk_bwd_dx
+// ---------------------------------------------------------------------------
+template <int Q, int N>
+struct DxLds {
+  using K = BwdCfg<Q>;
+  // g [64][N] for the state term, then dY and x rows [Q][64] each
+  static constexpr int R1 = (64 * N * 2 > Q * 256) ? 64 * N * 2 : Q * 256;
+  static constexpr int GS = 0, YS = 0, XS = Q * 128;
+  static constexpr int GT = R1;                        // masked C B^T tiles, bf16
+  static constexpr int CSS = GT + K::NTILE * 512;      // cs, dt, x.dU, T^S [Q] each
+  static constexpr int RP = CSS + 4 * Q * 4;           // per-wave rectangle-sum parts
+  static constexpr int RED = RP + K::NW * Q * 4;       // per-wave dy.x parts
+  static constexpr int BYTES = RED + 64;
+  static_assert(2 * Q * 128 <= BYTES, "setup slices fit in the same space");
+};
+
+// v + (v of the lane CTRL selects inside its 16-lane row), 0 where none.
+template <int CTRL>
+__device__ __forceinline__ float row_shr_add(float v) {
+  const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false);
+  return v + __builtin_bit_cast(float, s);
+}
+// Inclusive prefix sum over the 16 lanes of each row (lane order).
+__device__ __forceinline__ float row_scan16(float v) {
+  v = row_shr_add<0x111>(v);
+  v = row_shr_add<0x112>(v);
+  v = row_shr_add<0x114>(v);
+  return row_shr_add<0x118>(v);
+}
+// Value of the previous lane of the row (0 in its first lane).
+__device__ __forceinline__ float row_prev(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false));
+}
+
+// The log-decay gradient is formed without cancellation: for position k,
+//   d(A dt)_k = sum_{i >= k > j} T_ij + sum_{i >= k} T^h_i + sum_{j < k} T^S_j
+//               + 2^cs_last <g, h_start>,
+// T_ij = (M o CB)_ij dt_j (dy_i . x_j) for i > j (the in-chunk terms whose
+// decay spans position k), T^h_i = 2^cs_i dy_i . (h_start C_i) (from the
+// dB/dC kernel), T^S_j = dt_j x_j . dU^state_j.  Every sum is of terms of
+// one interaction each, so no large opposite contributions cancel.
+template <int Q, int N>
+__global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ dy, const bf16* __restrict__ Bm,
+    const bf16* __restrict__ Cm, const float* __restrict__ dA_cs, const float* __restrict__ dt_T,
+    const bf16* __restrict__ gst, const float* __restrict__ dots, const float* __restrict__ th,
+    const float* __restrict__ A, const float* __restrict__ D, bf16* __restrict__ dx,
+    bf16* __restrict__ ddt, float* __restrict__ dA_part, float* __restrict__ dD_part, int L, int H,
+    int G, int nc, int hpw, int slices, int wph) {
+  using K = BwdCfg<Q>;
+  using S = DxLds<Q, N>;
+  constexpr int P = 64, QT = K::QT, NW = K::NW, NT = K::NT, SLOTS = K::SLOTS, KN = N / 32;
+  constexpr int nT = N / 64;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+  int bid = blockIdx.x;
+  const int slice = bid % slices;
+  bid /= slices;
+  const int g = bid % G;
+  bid /= G;
+  const int c = bid % nc;
+  const int b = bid / nc;
+  const int HG = H / G;
+  const int h0 = g * HG + slice * hpw;
+  const int nh = min(hpw, HG - slice * hpw);
+  if (nh <= 0) return;  // whole workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int64_t tok0 = (int64_t)c * Q;
+  const int64_t valid = (int64_t)L - tok0;  // rows of this chunk inside the sequence
+  const int J[2] = {w, QT - 1 - w};
+
+  // ---- C B^T of the group (float32, this wave's triangle tiles) and the
+  // B operands of this wave's output columns for the state term.
+  f32x4 cb[SLOTS];
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) cb[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 Bop[2][KN];
+  {
+    const int L16 = lane & 15, grp = lane >> 4;
+    bf16* Cs = (bf16*)smem;
+    bf16* Bs = Cs + Q * 64;
+    const int64_t row0 = ((int64_t)b * L + tok0) * G + g;
+#pragma unroll
+    for (int ns = 0; ns < N / 64; ++ns) {
+      __syncthreads();
+      load_rows64<Q, NT>(Cs, Cm + row0 * N + ns * 64, (int64_t)G * N, valid);
+      load_rows64<Q, NT>(Bs, Bm + row0 * N + ns * 64, (int64_t)G * N, valid);
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < SLOTS; ++k) {
+        const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 a = *(const bf16x8*)(Cs + (ti * 16 + L16) * 64 + 32 * kk + 8 * grp);
+          const bf16x8 bb = *(const bf16x8*)(Bs + (tj * 16 + L16) * 64 + 32 * kk + 8 * grp);
+          cb[k] = mfma16x16x32(a, bb, cb[k]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          Bop[s][2 * ns + kk] = *(const bf16x8*)(Bs + (J[s] * 16 + L16) * 64 + 32 * kk + 8 * grp);
+    }
+    __syncthreads();
+  }
+
+  bf16* Gs = (bf16*)(smem + S::GS);
+  bf16* Ys = (bf16*)(smem + S::YS);
+  bf16* Xs = (bf16*)(smem + S::XS);
+  bf16* Gt = (bf16*)(smem + S::GT);
+  float* css = (float*)(smem + S::CSS);
+  float* dts = css + Q;
+  float* exs = dts + Q;
+  float* tsv = exs + Q;
+  float* rp = (float*)(smem + S::RP);
+  float* red = (float*)(smem + S::RED);
+
+  for (int hh = 0; hh < nh; ++hh) {
+    const int h = h0 + hh;
+    const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
+    const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;  // x, dy row tok0
+    {
+      const bf16* src = gst + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+      for (int s = tid; s < P * N / 8; s += NT) *(bf16x8*)(Gs + s * 8) = *(const bf16x8*)(src + s * 8);
+    }
+    const int64_t cb0 = (((int64_t)b * H + h) * nc + c) * Q;
+    for (int i = tid; i < Q; i += NT) {
+      css[i] = dA_cs[cb0 + i];
+      dts[i] = dt_T[cb0 + i];
+    }
+    for (int i = tid; i < NW * Q; i += NT) rp[i] = 0.f;
+    __syncthreads();
+
+    // ---- dU^T[p][j] state term for this wave's column tiles, scaled per
+    // column by 2^(cs_last - cs_j); T^S_j = dt_j x_j . dU^state_j
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) acc[s][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KN; ++ks)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const bf16x8 a = *(const bf16x8*)(Gs + (pt * 16 + L16) * N + 32 * ks + 8 * grp);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) acc[s][pt] = mfma16x16x32(a, Bop[s][ks], acc[s][pt]);
+      }
+    const float csL = css[Q - 1];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int j = J[s] * 16 + L16;
+      const float sc = fast_exp2(csL - css[j]);
+      float ts = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[s][pt][r] *= sc;
+        if (j < valid) {
+          const bf16x4 xv = *(const bf16x4*)(x + xrow0 + (int64_t)j * H * P + pt * 16 + 4 * grp);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ts += bf2f(xv[r]) * acc[s][pt][r];
+        }
+      }
+      ts += __shfl_xor(ts, 16, 64);
+      ts += __shfl_xor(ts, 32, 64);
+      if (grp == 0) tsv[j] = dts[j] * ts;
+    }
+    __syncthreads();  // g no longer needed: its space takes dY and x
+
+    load_rows64<Q, NT>(Ys, dy + xrow0, (int64_t)H * P, valid);
+    load_rows64<Q, NT>(Xs, x + xrow0, (int64_t)H * P, valid);
+    __syncthreads();
+
+    // ---- per triangle tile: masked, decayed C B^T to LDS (bfloat16) for the
+    // dU products, and T = (M o CB) dt_j (dY x^T) for the rectangle sums:
+    // row prefix sums along each row strip, column sums of those prefixes
+    float carry[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k) {
+      const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
+      if (k == w + 1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) carry[r] = 0.f;
+      }
+      f32x4 wv = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 a = *(const bf16x8*)(Ys + (ti * 16 + L16) * 64 + 32 * kk + 8 * grp);
+        const bf16x8 bb = *(const bf16x8*)(Xs + (tj * 16 + L16) * 64 + 32 * kk + 8 * grp);
+        wv = mfma16x16x32(a, bb, wv);
+      }
+      const int j = tj * 16 + L16;
+      const float csj = css[j], dtj = dts[j];
+      bf16* dst = Gt + tix_of(ti, tj) * 256 + 4 * grp * 16 + L16;
+      float col = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = ti * 16 + 4 * grp + r;
+        const float e = fast_exp2(fminf(css[i] - csj, 0.f));
+        const float gm = (i >= j) ? cb[k][r] * e : 0.f;
+        dst[r * 16] = f2bf(gm);
+        const float t = (i > j) ? gm * dtj * wv[r] : 0.f;
+        const float inc = row_scan16(t);
+        const float pm = carry[r] + row_prev(inc);  // sum_{j' < j} T[i][j'] over the row
+        carry[r] += __shfl(inc, 15, 16);
+        if (j <= i) col += pm;
+      }
+      col += __shfl_xor(col, 16, 64);
+      col += __shfl_xor(col, 32, 64);
+      if (grp == 0) rp[w * Q + j] += col;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+
+    // ---- causal part of dU^T
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int Js = J[s];
+      for (int kp = Js >> 1; kp < QT / 2; ++kp) {
+        const int ti = 2 * kp + (grp >> 1);
+        const bool live = ti >= Js;
+        const int tic = live ? ti : Js;
+        const bf16* gp = Gt + tix_of(tic, Js) * 256 + (8 * (grp & 1) + (L16 >> 2)) * 16 + 4 * (L16 & 3);
+        bf16x8 bop = cat(lds_read_tr(gp), lds_read_tr(gp + 64));
+        if (!live) bop = zero8();
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          const bf16* yp = Ys + (32 * kp + 8 * grp + (L16 >> 2)) * 64 + pt * 16 + 4 * (L16 & 3);
+          const bf16x8 aop = cat(lds_read_tr(yp), lds_read_tr(yp + 4 * 64));
+          acc[s][pt] = mfma16x16x32(aop, bop, acc[s][pt]);
+        }
+      }
+    }
+
+    // ---- epilogue: acc[s][pt][r] = dU[j = 16 J[s] + L16][p = 16 pt + 4 grp + r]
+    const float Ah = A[h];
+    const float Dh = D ? D[h] : 0.f;
+    float dd = 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int j = J[s] * 16 + L16;
+      float ex = 0.f;
+      if (j < valid) {
+        const float dtj = dts[j];
+        const int64_t off = xrow0 + (int64_t)j * H * P;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          const int p0 = pt * 16 + 4 * grp;
+          const bf16x4 xv = *(const bf16x4*)(x + off + p0);
+          const bf16x4 dv = *(const bf16x4*)(dy + off + p0);
+          bf16x4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float du = acc[s][pt][r], xf = bf2f(xv[r]), df = bf2f(dv[r]);
+            o[r] = f2bf(dtj * du + Dh * df);
+            ex += xf * du;
+            dd += df * xf;
+          }
+          *(bf16x4*)(dx + off + p0) = o;
+        }
+      }
+      ex += __shfl_xor(ex, 16, 64);
+      ex += __shfl_xor(ex, 32, 64);
+      if (grp == 0) exs[j] = ex;
+    }
+    dd = wave_sum(dd);
+    if (lane == 0) red[w] = dd;
+    __syncthreads();
+
+    // ---- d(A dt)_k, ddt, and the dA and dD parts (one wave)
+    if (w == 0) {
+      float dc = lane < wph ? dots[(((int64_t)b * H + h) * nc + c) * wph + lane] : 0.f;
+      dc = wave_sum(dc);
+      constexpr int E = Q / 64;
+      const float* thh = th + (((int64_t)b * nc + c) * H + h) * nT * Q;
+      float rk[E], sh[E], ps[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int k = lane * E + e;
+        float v = 0.f;
+        for (int i = 0; i < NW; ++i) v += rp[i * Q + k];
+        rk[e] = v;
+        float t = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < nT; ++nt) t += thh[nt * Q + k];
+        sh[e] = t;
+        ps[e] = tsv[k];
+      }
+      // suffix sums of T^h (over i >= k) and exclusive prefix sums of T^S
+      // (over j < k): inside the lane, then across lanes
+#pragma unroll
+      for (int e = E - 2; e >= 0; --e) sh[e] += sh[e + 1];
+      float run = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float v = ps[e];
+        ps[e] = run;
+        run += v;
+      }
+      float suf = sh[0], pre = run;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float a = __shfl_down(suf, off, 64);
+        const float bq = __shfl_up(pre, off, 64);
+        if (lane + off < 64) suf += a;
+        if (lane >= off) pre += bq;
+      }
+      float suf_after = __shfl_down(suf, 1, 64);
+      if (lane == 63) suf_after = 0.f;
+      float pre_before = __shfl_up(pre, 1, 64);
+      if (lane == 0) pre_before = 0.f;
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int k = lane * E + e;
+        const float da = rk[e] + sh[e] + suf_after + ps[e] + pre_before + dc;
+        if (k < valid) ddt[((int64_t)b * L + tok0 + k) * H + h] = f2bf(exs[k] + Ah * da);
+        part += dts[k] * da;
+      }
+      part = wave_sum(part);
+      if (lane == 0) {
+        float sd = 0.f;
+        for (int i = 0; i < NW; ++i) sd += red[i];
+        dA_part[((int64_t)b * nc + c) * H + h] = part;
+        dD_part[((int64_t)b * nc + c) * H + h] = sd;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// chunk_bwd_wsum: the group's summed, masked interaction matrix
+//     Wsum[i][j] = sum_h M_h[i, j] dt_h,j (dy_h,i . x_h,j),   i >= j
+// one workgroup per (batch, chunk, group), float32 accumulators over the
+// group's heads, written once as bfloat16 triangle tiles.  It does not depend
+// on the state size, so the dB/dC kernel's column tiles share it.
+// ---------------------------------------------------------------------------
+template <int Q>
+__global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ dy, const float* __restrict__ dA_cs,
+    const float* __restrict__ dt_T, bf16* __restrict__ wsum, int L, int H, int G, int nc) {
+  using K = BwdCfg<Q>;
+  constexpr int P = 64, QT = K::QT, NT = K::NT, SLOTS = K::SLOTS;
+  __shared__ __attribute__((aligned(16))) bf16 Ys[Q * 64];
+  __shared__ __attribute__((aligned(16))) bf16 Xs[Q * 64];
+  __shared__ float css[Q], dts[Q];
+
+  int bid = blockIdx.x;
+  const int g = bid % G;
+  bid /= G;
+  const int c = bid % nc;
+  const int b = bid / nc;
+  const int HG = H / G;
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int64_t tok0 = (int64_t)c * Q;
+  const int64_t valid = (int64_t)L - tok0;
+
+  f32x4 ws[SLOTS];
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) ws[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int hh = 0; hh < HG; ++hh) {
+    const int h = g * HG + hh;
+    const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
+    const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;
+    load_rows64<Q, NT>(Ys, dy + xrow0, (int64_t)H * P, valid);
+    load_rows64<Q, NT>(Xs, x + xrow0, (int64_t)H * P, valid);
+    const int64_t cb0 = (((int64_t)b * H + h) * nc + c) * Q;
+    for (int i = threadIdx.x; i < Q; i += NT) {
+      css[i] = dA_cs[cb0 + i];
+      dts[i] = dt_T[cb0 + i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k) {
+      const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
+      f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 a = *(const bf16x8*)(Ys + (ti * 16 + L16) * 64 + 32 * kk + 8 * grp);
+        const bf16x8 bb = *(const bf16x8*)(Xs + (tj * 16 + L16) * 64 + 32 * kk + 8 * grp);
+        a4 = mfma16x16x32(a, bb, a4);
+      }
+      const int j = tj * 16 + L16;
+      const float csj = css[j], dtj = dts[j];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = ti * 16 + 4 * grp + r;
+        const float e = fast_exp2(fminf(css[i] - csj, 0.f)) * dtj;
+        ws[k][r] += (i >= j ? e : 0.f) * a4[r];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  }
+
+  const int L16 = lane & 15, grp = lane >> 4;
+  bf16* out = wsum + (((int64_t)b * nc + c) * G + g) * (int64_t)(K::NTILE * 256);
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) {
+    bf16* dst = out + tix_of(slot_ti<QT>(w, k), slot_tj<QT>(w, k)) * 256 + 4 * grp * 16 + L16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[r * 16] = f2bf(ws[k][r]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// chunk_bwd_dbdc
+// ---------------------------------------------------------------------------
+// Q/16 waves: wave w owns output row tile w of dB and dC (row tile w has w+1
+// causal tiles for dC and Q/16-w for dB: Q/16+1 in all, for every wave).
+template <int Q>
+struct BcCfg {
+  static constexpr int QT = Q / 16, NW = QT, NT = 64 * NW;
+};
+
+template <int Q>
+struct BcLds {
+  using K = BwdCfg<Q>;
+  static constexpr int BS = 0;                 // B columns [Q][64]
+  static constexpr int CS = BS + Q * 128;      // C columns [Q][64]
+  static constexpr int HEAD = CS + Q * 128;    // per-head region
+  static constexpr int YS = HEAD;              // dY [Q][64]
+  static constexpr int XS = YS + Q * 128;      // x [Q][64]
+  static constexpr int HS = XS + Q * 128;      // h columns [64][64]
+  static constexpr int GS = HS + 8192;         // g columns [64][64]
+  static constexpr int CSS = GS + 8192;        // cs, dt [Q] each
+  static constexpr int BYTES = CSS + 2 * Q * 4;
+  static_assert(K::NTILE * 512 <= BYTES - HEAD, "summed W tiles fit in the per-head region");
+};
+
+template <int Q>
+__global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
+    const bf16* __restrict__ x, const bf16* __restrict__ dy, const bf16* __restrict__ Bm,
+    const bf16* __restrict__ Cm, const float* __restrict__ dA_cs, const float* __restrict__ dt_T,
+    const bf16* __restrict__ hst, const bf16* __restrict__ gst, const bf16* __restrict__ wsum,
+    bf16* __restrict__ dB, bf16* __restrict__ dC, float* __restrict__ th, int L, int H, int G,
+    int nc, int N, int64_t M, int nT) {
+  using K = BcCfg<Q>;
+  using S = BcLds<Q>;
+  constexpr int P = 64, QT = K::QT, NT = K::NT;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+  // The nT column tiles of one (batch, chunk, group) sit on one XCD
+  // (workgroup id mod 8) and share its L2 for the per-head rows.
+  const int64_t q = blockIdx.x;
+  const int64_t blk = q / (8 * nT), rem = q % (8 * nT);
+  const int nt = (int)(rem / 8);
+  const int64_t m = blk * 8 + rem % 8;
+  if (m >= M) return;  // whole workgroup
+  const int g = (int)(m % G);
+  const int64_t bc = m / G;
+  const int c = (int)(bc % nc);
+  const int b = (int)(bc / nc);
+  const int HG = H / G;
+
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int64_t tok0 = (int64_t)c * Q;
+  const int64_t valid = (int64_t)L - tok0;
+  const int R = w;  // output row tile
+
+  bf16* Bs = (bf16*)(smem + S::BS);
+  bf16* Cs = (bf16*)(smem + S::CS);
+  bf16* Ys = (bf16*)(smem + S::YS);
+  bf16* Xs = (bf16*)(smem + S::XS);
+  bf16* Hs = (bf16*)(smem + S::HS);
+  bf16* Gs = (bf16*)(smem + S::GS);
+  float* css = (float*)(smem + S::CSS);
+  float* dts = css + Q;
+
+  {
+    const int64_t row0 = ((int64_t)b * L + tok0) * G + g;
+    load_rows64<Q, NT>(Bs, Bm + row0 * N + nt * 64, (int64_t)G * N, valid);
+    load_rows64<Q, NT>(Cs, Cm + row0 * N + nt * 64, (int64_t)G * N, valid);
+  }
+
+  f32x4 accC[4], accB[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    accC[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accB[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int hh = 0; hh < HG; ++hh) {
+    const int h = g * HG + hh;
+    const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
+    const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;
+    load_rows64<Q, NT>(Ys, dy + xrow0, (int64_t)H * P, valid);
+    load_rows64<Q, NT>(Xs, x + xrow0, (int64_t)H * P, valid);
+    const int64_t st0 = (((int64_t)b * nc + c) * H + h) * (int64_t)P * N + nt * 64;
+    load_rows64<64, NT>(Hs, hst + st0, N, 64);
+    load_rows64<64, NT>(Gs, gst + st0, N, 64);
+    const int64_t cb0 = (((int64_t)b * H + h) * nc + c) * Q;
+    for (int i = threadIdx.x; i < Q; i += NT) {
+      css[i] = dA_cs[cb0 + i];
+      dts[i] = dt_T[cb0 + i];
+    }
+    __syncthreads();
+
+    // state terms of this wave's rows: 2^cs_i (dY h)[i, n] into dC and
+    // 2^(cs_last - cs_j) dt_j (X g)[j, n] into dB; T^h_i parts
+    {
+      const float csL = css[Q - 1];
+      bf16x8 aY[2], aX[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        aY[kk] = *(const bf16x8*)(Ys + (R * 16 + L16) * 64 + 32 * kk + 8 * grp);
+        aX[kk] = *(const bf16x8*)(Xs + (R * 16 + L16) * 64 + 32 * kk + 8 * grp);
+      }
+      float eC[4], eB[4], thr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = R * 16 + 4 * grp + r;
+        eC[r] = fast_exp2(css[i]);
+        eB[r] = fast_exp2(csL - css[i]) * dts[i];
+        thr[r] = 0.f;
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        f32x4 tc = f32x4{0.f, 0.f, 0.f, 0.f}, tb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int ro = (32 * kk + 8 * grp + (L16 >> 2)) * 64 + ct * 16 + 4 * (L16 & 3);
+          const bf16x8 hb = cat(lds_read_tr(Hs + ro), lds_read_tr(Hs + ro + 4 * 64));
+          const bf16x8 gb = cat(lds_read_tr(Gs + ro), lds_read_tr(Gs + ro + 4 * 64));
+          tc = mfma16x16x32(aY[kk], hb, tc);
+          tb = mfma16x16x32(aX[kk], gb, tb);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float vc = eC[r] * tc[r];
+          accC[ct][r] += vc;
+          accB[ct][r] += eB[r] * tb[r];
+          thr[r] += vc * bf2f(Cs[(R * 16 + 4 * grp + r) * 64 + ct * 16 + L16]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // T^h parts of this column tile: 2^cs_i dy_i . (h C_i) over its 64 columns
+      float* tho = th + ((((int64_t)b * nc + c) * H + h) * nT + nt) * Q + R * 16 + 4 * grp;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = thr[r];
+#pragma unroll
+        for (int mm = 1; mm < 16; mm <<= 1) v += __shfl_xor(v, mm, 64);
+        if (L16 == 0) tho[r] = v;
+      }
+    }
+    __syncthreads();
+  }
+
+  const int L16 = lane & 15, grp = lane >> 4;
+  // the group's summed W (bfloat16 triangle tiles) into LDS, then the
+  // products with B and C
+  bf16* Wt = (bf16*)(smem + S::HEAD);
+  {
+    const bf16* src = wsum + m * (int64_t)(BwdCfg<Q>::NTILE * 256);
+    for (int i = threadIdx.x; i < BwdCfg<Q>::NTILE * 32; i += NT)
+      *(bf16x8*)(Wt + i * 8) = *(const bf16x8*)(src + i * 8);
+  }
+  __syncthreads();
+
+  {
+    const int ti = R;  // dC rows: sum over j <= i
+    for (int kp = 0; kp <= (ti >> 1); ++kp) {
+      const int tj = 2 * kp + (grp >> 1);
+      const bool live = tj <= ti;
+      const int tjc = live ? tj : ti;
+      bf16x8 a = *(const bf16x8*)(Wt + tix_of(ti, tjc) * 256 + L16 * 16 + 8 * (grp & 1));
+      if (!live) a = zero8();
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const bf16* bp = Bs + (32 * kp + 8 * grp + (L16 >> 2)) * 64 + ct * 16 + 4 * (L16 & 3);
+        const bf16x8 bb = cat(lds_read_tr(bp), lds_read_tr(bp + 4 * 64));
+        accC[ct] = mfma16x16x32(a, bb, accC[ct]);
+      }
+    }
+    const int tj = R;  // dB rows: sum over i >= j
+    for (int kp = tj >> 1; kp < QT / 2; ++kp) {
+      const int tii = 2 * kp + (grp >> 1);
+      const bool live = tii >= tj;
+      const int tic = live ? tii : tj;
+      const bf16* wp = Wt + tix_of(tic, tj) * 256 + (8 * (grp & 1) + (L16 >> 2)) * 16 + 4 * (L16 & 3);
+      bf16x8 a = cat(lds_read_tr(wp), lds_read_tr(wp + 64));
+      if (!live) a = zero8();
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const bf16* cp = Cs + (32 * kp + 8 * grp + (L16 >> 2)) * 64 + ct * 16 + 4 * (L16 & 3);
+        const bf16x8 cc = cat(lds_read_tr(cp), lds_read_tr(cp + 4 * 64));
+        accB[ct] = mfma16x16x32(a, cc, accB[ct]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = R * 16 + 4 * grp + r;
+    if (i < valid) {
+      const int64_t o = (((int64_t)b * L + tok0 + i) * G + g) * N + nt * 64 + L16;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        dC[o + ct * 16] = f2bf(accC[ct][r]);
+        dB[o + ct * 16] = f2bf(accB[ct][r]);
+      }
+    }
+  }
+}
+
+// dA[h] and dD[h]: sums of the per-(batch, chunk) parts, one wave per head,
+// in a fixed order.
+__global__ void __launch_bounds__(64) bwd_param_sums_kernel(const float* __restrict__ dA_part,
+                                                            const float* __restrict__ dD_part,
+                                                            float* __restrict__ dA,
+                                                            float* __restrict__ dD, int64_t BC,
+                                                            int H) {
+  const int h = blockIdx.x;
+  float a = 0.f, d = 0.f;
+  for (int64_t u = threadIdx.x; u < BC; u += 64) {
+    a += dA_part[u * H + h];
+    d += dD_part[u * H + h];
+  }
+  a = wave_sum(a);
+  d = wave_sum(d);
+  if (threadIdx.x == 0) {
+    dA[h] = a;
+    if (dD) dD[h] = d;
+  }
+}
+
+int cu_count_bwd() {
+  static const int n = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    return v;
+  }();
+  return n;
+}
+
+template <int Q, int N>
+hipError_t launch_dx(const Dims& d, const void* x, const void* dy, const void* B, const void* C,
+                     const float* dA_cs, const float* dt_T, const void* gst, const float* dots,
+                     int wph, const float* th, const float* A, const float* D, void* dx,
+                     void* ddt, float* dA_part, float* dD_part, hipStream_t s) {
+  auto kern = chunk_bwd_dx_kernel<Q, N>;
+  constexpr int lds = DxLds<Q, N>::BYTES;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  const int64_t HG = d.H / d.G;
+  int64_t hpw = (d.B * d.nc * d.H) / cu_count_bwd();
+  if (hpw < 1) hpw = 1;
+  if (hpw > HG) hpw = HG;
+  const int64_t slices = (HG + hpw - 1) / hpw;
+  hpw = (HG + slices - 1) / slices;
+  const int64_t grid = d.B * d.nc * d.G * slices;
+  kern<<<(unsigned)grid, BwdCfg<Q>::NT, lds, s>>>(
+      (const bf16*)x, (const bf16*)dy, (const bf16*)B, (const bf16*)C, dA_cs, dt_T,
+      (const bf16*)gst, dots, th, A, D, (bf16*)dx, (bf16*)ddt, dA_part, dD_part, (int)d.L,
+      (int)d.H, (int)d.G, (int)d.nc, (int)hpw, (int)slices, wph);
+  return hipGetLastError();
+}
+
+template <int Q>
+hipError_t launch_dbdc(const Dims& d, const void* x, const void* dy, const void* B, const void* C,
+                       const float* dA_cs, const float* dt_T, const void* hst, const void* gst,
+                       void* wsum, void* dB, void* dC, float* th, hipStream_t s) {
+  chunk_bwd_wsum_kernel<Q><<<(unsigned)(d.B * d.nc * d.G), BwdCfg<Q>::NT, 0, s>>>(
+      (const bf16*)x, (const bf16*)dy, dA_cs, dt_T, (bf16*)wsum, (int)d.L, (int)d.H, (int)d.G,
+      (int)d.nc);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  auto kern = chunk_bwd_dbdc_kernel<Q>;
+  constexpr int lds = BcLds<Q>::BYTES;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  const int64_t M = d.B * d.nc * d.G;
+  const int nT = (int)(d.N / 64);
+  const int64_t grid = (M + 7) / 8 * 8 * nT;
+  kern<<<(unsigned)grid, BcCfg<Q>::NT, lds, s>>>(
+      (const bf16*)x, (const bf16*)dy, (const bf16*)B, (const bf16*)C, dA_cs, dt_T,
+      (const bf16*)hst, (const bf16*)gst, (const bf16*)wsum, (bf16*)dB, (bf16*)dC, th, (int)d.L,
+      (int)d.H, (int)d.G, (int)d.nc, (int)d.N, M, nT);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool backward_supported(const Dims& d) {
+  return d.bf16 && d.P == 64 && (d.N == 64 || d.N == 128 || d.N == 256) &&
+         (d.Q == 64 || d.Q == 128 || d.Q == 256);
+}
+
+hipError_t launch_chunk_bwd_dx(const Dims& d, const void* x, const void* dy, const void* B,
+                               const void* C, const float* dA_cs, const float* dt_T,
+                               const void* gst, const float* dots, int wph, const float* th,
+                               const float* A, const float* D, void* dx, void* ddt,
+                               float* dA_part, float* dD_part, hipStream_t s) {
+#define M2_DX(QQ, NN)                                                                       \
+  if (d.Q == QQ && d.N == NN)                                                               \
+    return launch_dx<QQ, NN>(d, x, dy, B, C, dA_cs, dt_T, gst, dots, wph, th, A, D, dx, ddt, \
+                             dA_part, dD_part, s);
+  M2_DX(64, 64) M2_DX(64, 128) M2_DX(64, 256)
+  M2_DX(128, 64) M2_DX(128, 128) M2_DX(128, 256)
+  M2_DX(256, 64) M2_DX(256, 128) M2_DX(256, 256)
+#undef M2_DX
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_bwd_dbdc(const Dims& d, const void* x, const void* dy, const void* B,
+                                 const void* C, const float* dA_cs, const float* dt_T,
+                                 const void* hst, const void* gst, void* wsum, void* dB,
+                                 void* dC, float* th, hipStream_t s) {
+  switch (d.Q) {
+    case 64: return launch_dbdc<64>(d, x, dy, B, C, dA_cs, dt_T, hst, gst, wsum, dB, dC, th, s);
+    case 128: return launch_dbdc<128>(d, x, dy, B, C, dA_cs, dt_T, hst, gst, wsum, dB, dC, th, s);
+    case 256: return launch_dbdc<256>(d, x, dy, B, C, dA_cs, dt_T, hst, gst, wsum, dB, dC, th, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_param_sums(const Dims& d, const float* dA_part, const float* dD_part,
+                                 float* dA, float* dD, hipStream_t s) {
+  bwd_param_sums_kernel<<<(unsigned)d.H, 64, 0, s>>>(dA_part, dD_part, dA, dD, d.B * d.nc,
+                                                     (int)d.H);
+  return hipGetLastError();
+}
+
+}  // namespace m2

@@ -14,6 +14,12 @@
 // next head's bytes have been waited for, so they drain during the next
 // head's work.
 //
+// The same kernel forms the adjoint chunk states of the backward pass (ADJ):
+//     E[p, n] = sum_i 2^cs[i] dy[i, p] C[i, n]
+// the gradient that chunk's outputs send back into its start state, from the
+// state term y_i += 2^cs[i] (h C_i) of the forward pass; only the row weights
+// differ (rows past the sequence end weigh 0).
+//
 // Layout: N/32 waves; wave w owns the 32 state columns n0 = 32 w .. 32 w + 31
 // as NTW = 2 MFMA tiles, MFMA row m of tile nt standing for
 // n = n0 + 4 NTW (m/4) + 4 nt + m%4, so each lane stores 4 NTW consecutive n
@@ -68,7 +74,7 @@ __device__ __forceinline__ void load_x(uint32_t buf, const bf16* __restrict__ x,
   if (w < 2 && lane < Q / 4) dma16((w == 0 ? dA_cs : dt_T) + cb + lane * 4, cs + w * K::CS_BYTES);
 }
 
-template <int P, int Q, int N>
+template <int P, int Q, int N, bool ADJ>
 __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chunk_state_grouped_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ dA_cs,
     const float* __restrict__ dt_T, float* __restrict__ states, int L, int H, int G, int nc,
@@ -150,7 +156,10 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
         const int s = tid + K::NT * i;
         const int r = s >> 3;
         v[i] = *(const bf16x8*)(cur + s * 16);
-        wr[i] = fast_exp2(cs_last - css[r]) * dts[r];
+        if constexpr (ADJ)
+          wr[i] = (tok0 + r < L) ? fast_exp2(css[r]) : 0.f;
+        else
+          wr[i] = fast_exp2(cs_last - css[r]) * dts[r];
       }
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
@@ -207,11 +216,11 @@ int cu_count_state() {
   return n;
 }
 
-template <int P, int Q, int N>
+template <int P, int Q, int N, bool ADJ>
 hipError_t launch_grouped(const Dims& d, const void* x, const void* B, const float* dA_cs,
                           const float* dt_T, float* states, hipStream_t s) {
   using K = SCfg<P, Q, N>;
-  auto kern = chunk_state_grouped_kernel<P, Q, N>;
+  auto kern = chunk_state_grouped_kernel<P, Q, N, ADJ>;
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS);
   if (attr != hipSuccess) return attr;
@@ -230,13 +239,24 @@ hipError_t launch_grouped(const Dims& d, const void* x, const void* B, const flo
   return hipGetLastError();
 }
 
-template <int Q>
+template <int Q, bool ADJ>
 hipError_t launch_grouped_n(const Dims& d, const void* x, const void* B, const float* dA_cs,
                             const float* dt_T, float* states, hipStream_t s) {
   switch (d.N) {
-    case 64: return launch_grouped<64, Q, 64>(d, x, B, dA_cs, dt_T, states, s);
-    case 128: return launch_grouped<64, Q, 128>(d, x, B, dA_cs, dt_T, states, s);
-    case 256: return launch_grouped<64, Q, 256>(d, x, B, dA_cs, dt_T, states, s);
+    case 64: return launch_grouped<64, Q, 64, ADJ>(d, x, B, dA_cs, dt_T, states, s);
+    case 128: return launch_grouped<64, Q, 128, ADJ>(d, x, B, dA_cs, dt_T, states, s);
+    case 256: return launch_grouped<64, Q, 256, ADJ>(d, x, B, dA_cs, dt_T, states, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool ADJ>
+hipError_t launch_grouped_q(const Dims& d, const void* x, const void* B, const float* dA_cs,
+                            const float* dt_T, float* states, hipStream_t s) {
+  switch (d.Q) {
+    case 64: return launch_grouped_n<64, ADJ>(d, x, B, dA_cs, dt_T, states, s);
+    case 128: return launch_grouped_n<128, ADJ>(d, x, B, dA_cs, dt_T, states, s);
+    case 256: return launch_grouped_n<256, ADJ>(d, x, B, dA_cs, dt_T, states, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -251,12 +271,13 @@ bool grouped_state_supported(const Dims& d) {
 hipError_t launch_chunk_state_grouped(const Dims& d, const void* x, const void* B,
                                       const float* dA_cs, const float* dt_T, float* states,
                                       hipStream_t s) {
-  switch (d.Q) {
-    case 64: return launch_grouped_n<64>(d, x, B, dA_cs, dt_T, states, s);
-    case 128: return launch_grouped_n<128>(d, x, B, dA_cs, dt_T, states, s);
-    case 256: return launch_grouped_n<256>(d, x, B, dA_cs, dt_T, states, s);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_grouped_q<false>(d, x, B, dA_cs, dt_T, states, s);
+}
+
+hipError_t launch_chunk_state_adjoint(const Dims& d, const void* dy, const void* C,
+                                      const float* dA_cs, const float* dt_T, float* states,
+                                      hipStream_t s) {
+  return launch_grouped_q<true>(d, dy, C, dA_cs, dt_T, states, s);
 }
 
 }  // namespace m2

@@ -37,6 +37,33 @@ hipError_t launch_chunk_scan_grouped(const Dims& d, const void* x, const void* B
                                      const float* dA_cs, const float* dt_T, const void* hst,
                                      const float* D, void* y, hipStream_t s);
 
+// Backward pass (bfloat16, P = 64, N in {64, 128, 256}, Q in {64, 128, 256}).
+bool backward_supported(const Dims& d);
+// E[B,nc,H,P,N] f32: per-chunk adjoint states sum_i 2^cs_i dy_i C_i^T.
+hipError_t launch_chunk_state_adjoint(const Dims& d, const void* dy, const void* C,
+                                      const float* dA_cs, const float* dt_T, float* states,
+                                      hipStream_t s);
+// Reverse jump over E: gst[B,nc,H,P,N] bf16 (gradient at each chunk's end),
+// dh0 (nullable), dots[B,H,nc,wph] (parts of 2^cs_last <g_c, h_c>).
+int64_t state_reverse_waves_per_head(const Dims& d);
+hipError_t launch_state_passing_reverse(const Dims& d, const float* E, const float* dA_cs,
+                                        const float* dfinal, const void* hst, void* gst,
+                                        float* dh0, float* dots, hipStream_t s);
+// dB, dC, and th[B,nc,H,N/64,Q]: per state-column tile parts of
+// 2^cs_i dy_i . (h_c C_i), the carried-state term of y_i weighted by dy_i.
+// wsum: [B,nc,G] blocks of Q(Q+16)/2 bf16 (the group's summed W triangle).
+hipError_t launch_chunk_bwd_dbdc(const Dims& d, const void* x, const void* dy, const void* B,
+                                 const void* C, const float* dA_cs, const float* dt_T,
+                                 const void* hst, const void* gst, void* wsum, void* dB,
+                                 void* dC, float* th, hipStream_t s);
+hipError_t launch_chunk_bwd_dx(const Dims& d, const void* x, const void* dy, const void* B,
+                               const void* C, const float* dA_cs, const float* dt_T,
+                               const void* gst, const float* dots, int wph, const float* th,
+                               const float* A, const float* D, void* dx, void* ddt,
+                               float* dA_part, float* dD_part, hipStream_t s);
+hipError_t launch_bwd_param_sums(const Dims& d, const float* dA_part, const float* dD_part,
+                                 float* dA, float* dD, hipStream_t s);
+
 // One-token recurrent step, in place on the float32 state [B,H,P,N];
 // x, y [B,H,P], dt [B,H], B, C [B,G,N].
 hipError_t launch_decode_step(const Dims& d, const void* x, const void* dt, const float* A,

@@ -73,7 +73,96 @@ __global__ void __launch_bounds__(kThreads) state_passing_kernel(
   if (final_state) ((V*)final_state)[bh * PNv + gid] = run;
 }
 
+// Backward pass: the same jump run in reverse chunk order on the adjoint.
+// With r_c the gradient of the loss with respect to the start state of
+// chunk c, r_nc = dfinal and r_c = 2^cs_last(c) r_{c+1} + E_c, where E_c is
+// chunk c's adjoint chunk state.  Writes g_c = r_{c+1} (the gradient reaching
+// chunk c's end state) as bfloat16, dh0 = r_0 in float32, and for every chunk
+// the per-wavefront parts of 2^cs_last(c) <g_c, h_c>: the end-of-chunk
+// gradient times the decayed start state, the part of the derivative with
+// respect to the chunk's log decays that flows through the carried state.
+// h_c is the forward pass's bfloat16 start state of chunk c.
+__global__ void __launch_bounds__(kThreads) state_passing_reverse_kernel(
+    const f32x4* __restrict__ E, const float* __restrict__ dA_cs,
+    const f32x4* __restrict__ dfinal, const bf16x4* __restrict__ hst, bf16x4* __restrict__ gst,
+    f32x4* __restrict__ dh0, float* __restrict__ dots, int64_t H, int64_t PNv,
+    int64_t blocks_per_head, int nc, int Q) {
+  const int64_t bh = (int64_t)blockIdx.x / blocks_per_head;  // b * H + h
+  const int64_t blk = (int64_t)blockIdx.x % blocks_per_head;
+  const int64_t gid = blk * kThreads + threadIdx.x;
+  const bool live = gid < PNv;  // dead lanes still take part in the wave sums
+  const int64_t g = live ? gid : 0;
+  const int64_t b = bh / H, h = bh % H;
+  const int64_t chunk_stride = H * PNv;
+  const int64_t base = (b * nc * H + h) * PNv + g;
+  const float* cs_last = dA_cs + bh * (int64_t)nc * Q + (Q - 1);
+  const int64_t wph = blocks_per_head * (kThreads / 64);
+  float* dot_out = dots + bh * (int64_t)nc * wph + blk * (kThreads / 64) + (threadIdx.x >> 6);
+
+  f32x4 run = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (dfinal && live) run = dfinal[bh * PNv + g];
+
+  // slot k of a ring holds chunk nc-1-(c0+k): its E and its start state
+  f32x4 eb[kDepth];
+  bf16x4 hb[kDepth];
+#pragma unroll
+  for (int k = 0; k < kDepth; ++k) {
+    const int c = nc - 1 - k;
+    if (c >= 0) {
+      eb[k] = __builtin_nontemporal_load(E + base + (int64_t)c * chunk_stride);
+      hb[k] = hst[base + (int64_t)c * chunk_stride];
+    }
+  }
+  for (int c0 = 0; c0 < nc; c0 += kDepth) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      const int c = nc - 1 - (c0 + k);
+      if (c >= 0) {
+        const f32x4 cur = eb[k];
+        f32x4 hc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hc[e] = bf2f(hb[k][e]);
+        const int cn = c - kDepth;  // chunk this slot holds next
+        if (cn >= 0) {
+          eb[k] = __builtin_nontemporal_load(E + base + (int64_t)cn * chunk_stride);
+          hb[k] = hst[base + (int64_t)cn * chunk_stride];
+        }
+        if (live) {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = f2bf(run[e]);
+          gst[base + (int64_t)c * chunk_stride] = o;
+        }
+        const float decay = exp2f(cs_last[(int64_t)c * Q]);
+        float part = live ? run[0] * hc[0] + run[1] * hc[1] + run[2] * hc[2] + run[3] * hc[3] : 0.f;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+        if ((threadIdx.x & 63) == 0) dot_out[(int64_t)c * wph] = decay * part;
+        run = decay * run + cur;
+      }
+    }
+  }
+  if (dh0 && live) dh0[bh * PNv + g] = run;
+}
+
 }  // namespace
+
+int64_t state_reverse_waves_per_head(const Dims& d) {
+  const int64_t PNv = d.P * d.N / 4;
+  return (PNv + kThreads - 1) / kThreads * (kThreads / 64);
+}
+
+hipError_t launch_state_passing_reverse(const Dims& d, const float* E, const float* dA_cs,
+                                        const float* dfinal, const void* hst, void* gst,
+                                        float* dh0, float* dots, hipStream_t s) {
+  const int64_t PN = d.P * d.N;
+  if (PN % 4 != 0) return hipErrorInvalidValue;
+  const int64_t PNv = PN / 4, bph = (PNv + kThreads - 1) / kThreads;
+  state_passing_reverse_kernel<<<(unsigned)(d.B * d.H * bph), kThreads, 0, s>>>(
+      (const f32x4*)E, dA_cs, (const f32x4*)dfinal, (const bf16x4*)hst, (bf16x4*)gst,
+      (f32x4*)dh0, dots, d.H, PNv, bph, (int)d.nc, (int)d.Q);
+  return hipGetLastError();
+}
 
 hipError_t launch_state_passing(const Dims& d, float* states, const float* dA_cs,
                                 const float* init, float* final_state, hipStream_t s) {

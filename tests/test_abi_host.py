@@ -128,3 +128,35 @@ def test_decode_step_checks_on_host():
     assert rc == m2.MAMBA2_ERR_ALIGN and "state" in m2.mamba2_last_error()
     rc = lib.mamba2_decode_step(ctypes.byref(d1), ok, ok, ok, ok, ok, ok + 4, ok, ok, 0)
     assert rc == m2.MAMBA2_ERR_ALIGN and "D" in m2.mamba2_last_error()
+
+
+def test_backward_checks_on_host():
+    lib = m2._lib
+    ok = 1 << 20
+    big = 1 << 40
+    d = _dims()
+    assert m2.mamba2_ssd_backward_workspace_bytes(d) > m2.mamba2_ssd_workspace_bytes(d)
+
+    def call(dims, **over):
+        args = dict(x=ok, dt=ok, A=ok, B=ok, C=ok, D=None, h0=None, dy=ok, dfin=None, dx=ok,
+                    ddt=ok, dA=ok, dB=ok, dC=ok, dD=None, dinit=None, ws=ok, wsb=big)
+        args.update(over)
+        return lib.mamba2_ssd_backward(ctypes.byref(dims), *args.values(), 0)
+
+    # float32 and headdim 32 are valid forward sizes the backward does not cover
+    for kw in (dict(dtype=m2.MAMBA2_DTYPE_F32, headdim=16, dstate=16, nheads=2, chunk_size=64),
+               dict(headdim=32), dict(dstate=512)):
+        dd = _dims(**kw)
+        assert m2.mamba2_validate(dd) == m2.MAMBA2_OK
+        assert m2.mamba2_ssd_backward_workspace_bytes(dd) == 0
+        assert call(dd) == m2.MAMBA2_ERR_UNSUPPORTED and "backward" in m2.mamba2_last_error()
+    assert call(d, dy=None) == m2.MAMBA2_ERR_NULL and "dy" in m2.mamba2_last_error()
+    assert call(d, dB=ok + 2) == m2.MAMBA2_ERR_ALIGN and "dB" in m2.mamba2_last_error()
+    # dD is required exactly when D is given
+    assert call(d, D=ok) == m2.MAMBA2_ERR_NULL and "dD" in m2.mamba2_last_error()
+    assert call(d, dfin=ok + 8) == m2.MAMBA2_ERR_ALIGN and "dfinal" in m2.mamba2_last_error()
+    assert call(d, ws=None) == m2.MAMBA2_ERR_WORKSPACE
+    assert call(d, ws=ok + 16) == m2.MAMBA2_ERR_WORKSPACE
+    need = m2.mamba2_ssd_backward_workspace_bytes(d)
+    assert call(d, wsb=need - 1) == m2.MAMBA2_ERR_WORKSPACE
+    assert "needed" in m2.mamba2_last_error()
