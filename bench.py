@@ -7,6 +7,8 @@ kernel (per-kernel durations measured here with HIP events on the launch
 stream) and the CPU oracle's throughput on the host as a reported baseline.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload long_L64k_N256]
+    python bench.py --backward      (the backward pass on the same workload)
+    python bench.py --decode-batch B (the one-token recurrent step)
 """
 from __future__ import annotations
 
@@ -74,12 +76,21 @@ def main():
     ap.add_argument("--decode-batch", type=int, default=0,
                     help="only measure the one-token recurrent step at this batch size "
                          "(H=32, P=64, N=256, bf16)")
+    ap.add_argument("--backward", action="store_true",
+                    help="only measure the backward pass (mamba2_ssd_backward) on the workload")
     args = ap.parse_args()
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
         return
     if args.decode_batch:
         decode_bench(args)
+        return
+    if args.backward:
+        if args.gpus != 1:
+            print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                              "n_gpus": args.gpus}))
+            sys.exit(2)
+        backward_bench(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
@@ -176,28 +187,44 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def csrc_digest():
-    """sha256 over the HIP sources (file names and bytes, in name order)."""
+# Source files that define each stage's kernel (with the shared helpers): a
+# profile's byte counts stand for the kernel only while these are unchanged.
+KERNEL_SOURCES = {
+    "chunk_cumsum": ("chunk_cumsum.hip", "common.h"),
+    "chunk_state": ("chunk_state_grouped.hip", "common.h"),
+    "state_passing": ("state_passing.hip", "common.h"),
+    "chunk_scan": ("chunk_scan_grouped.hip", "common.h"),
+    "adjoint_state": ("chunk_state_grouped.hip", "common.h"),
+    "reverse_pass": ("state_passing.hip", "common.h"),
+    "dB_dC": ("chunk_bwd.hip", "common.h"),
+    "dx": ("chunk_bwd.hip", "common.h"),
+    "param_sums": ("chunk_bwd.hip", "common.h"),
+}
+
+
+def sources_digest(stage):
+    """sha256 over the files that define `stage`'s kernel (names and bytes)."""
     import hashlib
     d = os.path.join(ROOT, "state_space_sequence_02_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
+    for f in KERNEL_SOURCES[stage]:
         h.update(f.encode())
         with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def profiled_traffic(workload, stage):
+def profiled_traffic(workload, stage, direction="forward"):
     """HBM bytes per launch of `stage` from the committed rocprofv3 summary of
     this workload (FETCH_SIZE and WRITE_SIZE, each scaled by the copy-kernel
-    calibration), or None when there is none or the kernels changed since."""
-    path = os.path.join(ROOT, "profiles", f"ssd_forward_{workload}.md")
+    calibration), or None when there is none or the kernel's sources changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"ssd_{direction}_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"csrc-sha256: ([0-9a-f]{64})", text)
-    if not m or m.group(1) != csrc_digest():
+    m = re.search(rf"sources-sha256 {stage}: ([0-9a-f]{{64}})", text)
+    if not m or m.group(1) != sources_digest(stage):
         return None
     for line in text.splitlines():
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
@@ -263,6 +290,126 @@ def decode_bench(args):
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None},
     }), flush=True)
+
+
+BWD_STAGES = ("chunk_cumsum", "chunk_state", "state_passing", "adjoint_state", "reverse_pass",
+              "dB_dC", "dx", "param_sums")
+
+
+def backward_model(w):
+    """Algorithmic flops and HBM bytes per launch of each backward stage
+    (inputs read once, outputs written once; flops over the causal triangle,
+    the group-shared products once per (chunk, group))."""
+    B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
+    nc = w.nchunks
+    tok, csb = B * L, B * H * nc * Q * 4
+    st = B * nc * H * P * N * 4
+    hs = st // 2
+    fin = B * H * P * N * 4
+    x = tok * H * P * 2
+    bc = tok * G * N * 2
+    th = B * nc * H * (N // 64) * Q * 4
+    fwd = stage_model(w)
+    m = {k: fwd[k] for k in ("chunk_cumsum", "chunk_state", "state_passing")}
+    m["adjoint_state"] = dict(flops=2 * N * P * tok * H, bytes=x + bc + 2 * csb + st)
+    m["reverse_pass"] = dict(flops=2 * st // 4 + 2 * st // 4,
+                             bytes=st + hs + B * H * nc * 4 + 2 * fin + hs)
+    m["dB_dC"] = dict(flops=tok * H * ((Q + 1) * P + 4 * P * N) + tok * G * 2 * (Q + 1) * N,
+                      bytes=2 * x + 2 * bc + 2 * hs + 2 * csb + 2 * bc + th)
+    m["dx"] = dict(flops=tok * G * (Q + 1) * N + tok * H * (2 * P * N + 2 * (Q + 1) * P),
+                   bytes=2 * x + 2 * bc + hs + 2 * csb + th + x + tok * H * 2)
+    m["param_sums"] = dict(flops=4 * B * nc * H, bytes=2 * B * nc * H * 4 + 2 * H * 4)
+    return m
+
+
+def backward_bench(args):
+    """Backward pass over the workload: tokens/s of one mamba2_ssd_backward
+    (it recomputes the forward's chunk states inside), per-stage times from
+    HIP events on the launch stream, the dominant kernel's roofline, and the
+    CPU oracle's back-propagation through the recurrence as the baseline."""
+    import torch
+
+    import ssd_inputs
+    import state_space_sequence_02_amd as m2
+
+    w = ssd_inputs.WORKLOADS[args.workload]
+    inp = ssd_inputs.make_inputs(w)
+    cot = ssd_inputs.make_cotangents(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    dy, dfin = cot["dy"].to(dev), cot["dfinal"].to(dev)
+    dims = m2.dims_of(g["x"], g["B"], w.chunk_size)
+    need = m2.mamba2_ssd_backward_workspace_bytes(dims)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    o = {"dx": torch.empty_like(g["x"]), "ddt": torch.empty_like(g["dt"]),
+         "dA": torch.empty_like(g["A"]), "dB": torch.empty_like(g["B"]),
+         "dC": torch.empty_like(g["C"]), "dD": torch.empty_like(g["D"]),
+         "dinit": torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32,
+                              device=dev)}
+    stream = torch.cuda.current_stream()
+    a = (dims, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], g["init_state"], dy, dfin,
+         o["dx"], o["ddt"], o["dA"], o["dB"], o["dC"], o["dD"], o["dinit"], ws, need, stream)
+
+    for _ in range(args.warmup):
+        m2.mamba2_ssd_backward(*a)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        m2.mamba2_ssd_backward(*a)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    ssum = [0.0] * len(BWD_STAGES)
+    for _ in range(args.steps):
+        ssum = [u + v for u, v in zip(ssum, m2.mamba2_ssd_backward_profile(*a))]
+    stage_ms = {s: ssum[i] / args.steps for i, s in enumerate(BWD_STAGES)}
+    model = backward_model(w)
+    dom = max(BWD_STAGES, key=lambda s: stage_ms[s])
+    dm = model[dom]
+    bound = "hbm" if dm["flops"] / dm["bytes"] < RIDGE else "mfma"
+    if bound == "hbm":
+        achieved, peak, unit = dm["bytes"] / (stage_ms[dom] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = dm["flops"] / (stage_ms[dom] * 1e-3) / 1e12
+        peak, unit = BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
+    stages = {}
+    for s in BWD_STAGES:
+        t = stage_ms[s] * 1e-3
+        stages[s] = {"ms": round(stage_ms[s], 4),
+                     "GB/s": round(model[s]["bytes"] / t / 1e9, 1),
+                     "TFLOP/s": round(model[s]["flops"] / t / 1e12, 2),
+                     "hbm_frac": round(model[s]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 3)}
+    out = {
+        "metric": "SSD backward tokens/s at L=64K,N=256 on 1 MI355X (forward states recomputed)",
+        "value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk_size": w.chunk_size, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak,
+                     "traffic": profiled_traffic(w.name, dom, "backward"),
+                     "algorithmic_bytes": dm["bytes"], "algorithmic_flops": dm["flops"]},
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        Ls = w.seqlen if args.cpu_tokens <= 0 else min(w.seqlen, args.cpu_tokens)
+        oc = {k: (None if v is None else v[:, :Ls].float().numpy() if k in ("x", "dt", "B", "C")
+                  else v.float().numpy()) for k, v in inp.items()}
+        t0 = time.perf_counter()
+        oracle.ssd_backward(oc["x"], oc["dt"], oc["A"], oc["B"], oc["C"], oc["D"],
+                            oc["init_state"], cot["dy"][:, :Ls].float().numpy(),
+                            cot["dfinal"].numpy(), chunk_size=w.chunk_size)
+        sec = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": w.batch * Ls / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": sec,
+            "sample": f"first {Ls} of {w.seqlen} tokens, all {w.nheads} heads, batch {w.batch}"}
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(inp, w, tokens_per_head):

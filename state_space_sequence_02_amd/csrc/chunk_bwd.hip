@@ -85,16 +85,41 @@ __device__ __forceinline__ int slot_ti(int w, int k) { return k <= w ? w : QT - 
 template <int QT>
 __device__ __forceinline__ int slot_tj(int w, int k) { return k <= w ? k : k - w - 1; }
 
-// rows [Q][64] of bfloat16 into LDS; row r comes from src + r * stride (in
-// elements), rows at or past `valid` are zero.
+// LDS tiles are stored with their 16-byte chunks permuted per row so that
+// the 16 rows an MFMA operand read touches fall on distinct banks.
+// Element (r, col) of a [rows][64] tile (128-byte rows, 8 chunks):
+__device__ __forceinline__ int t64(int r, int col) {
+  return r * 64 + ((((col >> 3) ^ (r >> 1)) & 7) << 3) + (col & 7);
+}
+// Element (r, col) of a [64][N] tile (N/8 chunks per row).
+template <int N>
+__device__ __forceinline__ int tN(int r, int col) {
+  if constexpr (N >= 128)
+    return r * N + (((col >> 3) ^ (r & 15)) << 3) + (col & 7);
+  else
+    return t64(r, col);
+}
+
+// rows [ROWS][64] of bfloat16 into an LDS tile; row r comes from
+// src + r * stride (in elements), rows at or past `valid` are zero.  Every
+// load of the thread is issued before its first LDS write, so the tile costs
+// one memory latency rather than one per 16-byte piece.
 template <int ROWS, int NT>
 __device__ __forceinline__ void load_rows64(bf16* dst, const bf16* __restrict__ src,
                                             int64_t stride, int64_t valid) {
-  for (int s = threadIdx.x; s < ROWS * 8; s += NT) {
+  constexpr int IT = (ROWS * 8 + NT - 1) / NT;
+  bf16x8 v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int s = threadIdx.x + it * NT;
     const int r = s >> 3, ch = s & 7;
-    bf16x8 v = zero8();
-    if (r < valid) v = *(const bf16x8*)(src + (int64_t)r * stride + ch * 8);
-    *(bf16x8*)(dst + r * 64 + ch * 8) = v;
+    v[it] = zero8();
+    if (s < ROWS * 8 && r < valid) v[it] = *(const bf16x8*)(src + (int64_t)r * stride + ch * 8);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int s = threadIdx.x + it * NT;
+    if (s < ROWS * 8) *(bf16x8*)(dst + t64(s >> 3, (s & 7) * 8)) = v[it];
   }
 }
 
@@ -108,8 +133,8 @@ struct DxLds {
   static constexpr int R1 = (64 * N * 2 > Q * 256) ? 64 * N * 2 : Q * 256;
   static constexpr int GS = 0, YS = 0, XS = Q * 128;
   static constexpr int GT = R1;                        // masked C B^T tiles, bf16
-  static constexpr int CSS = GT + K::NTILE * 512;      // cs, dt, x.dU, T^S [Q] each
-  static constexpr int RP = CSS + 4 * Q * 4;           // per-wave rectangle-sum parts
+  static constexpr int CSS = GT + K::NTILE * 512;      // cs, dt, x.dU, T^S, T^h [Q] each
+  static constexpr int RP = CSS + 5 * Q * 4 + 16;      // per-wave rectangle-sum parts
   static constexpr int RED = RP + K::NW * Q * 4;       // per-wave dy.x parts
   static constexpr int BYTES = RED + 64;
   static_assert(2 * Q * 128 <= BYTES, "setup slices fit in the same space");
@@ -196,8 +221,8 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
         const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 a = *(const bf16x8*)(Cs + (ti * 16 + L16) * 64 + 32 * kk + 8 * grp);
-          const bf16x8 bb = *(const bf16x8*)(Bs + (tj * 16 + L16) * 64 + 32 * kk + 8 * grp);
+          const bf16x8 a = *(const bf16x8*)(Cs + t64(ti * 16 + L16, 32 * kk + 8 * grp));
+          const bf16x8 bb = *(const bf16x8*)(Bs + t64(tj * 16 + L16, 32 * kk + 8 * grp));
           cb[k] = mfma16x16x32(a, bb, cb[k]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -206,7 +231,7 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-          Bop[s][2 * ns + kk] = *(const bf16x8*)(Bs + (J[s] * 16 + L16) * 64 + 32 * kk + 8 * grp);
+          Bop[s][2 * ns + kk] = *(const bf16x8*)(Bs + t64(J[s] * 16 + L16, 32 * kk + 8 * grp));
     }
     __syncthreads();
   }
@@ -219,6 +244,8 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
   float* dts = css + Q;
   float* exs = dts + Q;
   float* tsv = exs + Q;
+  float* ths = tsv + Q;
+  float* dcs = ths + Q;  // one value: 2^cs_last <g, h_start>
   float* rp = (float*)(smem + S::RP);
   float* red = (float*)(smem + S::RED);
 
@@ -228,7 +255,16 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
     const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;  // x, dy row tok0
     {
       const bf16* src = gst + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
-      for (int s = tid; s < P * N / 8; s += NT) *(bf16x8*)(Gs + s * 8) = *(const bf16x8*)(src + s * 8);
+      constexpr int IT = P * N / 8 / NT;
+      static_assert(P * N / 8 % NT == 0, "g tile splits evenly over the threads");
+      bf16x8 v[IT];
+#pragma unroll
+      for (int it = 0; it < IT; ++it) v[it] = *(const bf16x8*)(src + (tid + it * NT) * 8);
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int s = tid + it * NT;
+        *(bf16x8*)(Gs + tN<N>(s / (N / 8), (s % (N / 8)) * 8)) = v[it];
+      }
     }
     const int64_t cb0 = (((int64_t)b * H + h) * nc + c) * Q;
     for (int i = tid; i < Q; i += NT) {
@@ -236,6 +272,20 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
       dts[i] = dt_T[cb0 + i];
     }
     for (int i = tid; i < NW * Q; i += NT) rp[i] = 0.f;
+    {
+      const float* thh = th + (((int64_t)b * nc + c) * H + h) * nT * Q;
+      for (int i = tid; i < Q; i += NT) {
+        float t = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < nT; ++nt) t += thh[nt * Q + i];
+        ths[i] = t;
+      }
+      if (w == NW - 1) {
+        float dc = lane < wph ? dots[(((int64_t)b * H + h) * nc + c) * wph + lane] : 0.f;
+        dc = wave_sum(dc);
+        if (lane == 0) dcs[0] = dc;
+      }
+    }
     __syncthreads();
 
     // ---- dU^T[p][j] state term for this wave's column tiles, scaled per
@@ -249,35 +299,40 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
     for (int ks = 0; ks < KN; ++ks)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const bf16x8 a = *(const bf16x8*)(Gs + (pt * 16 + L16) * N + 32 * ks + 8 * grp);
+        const bf16x8 a = *(const bf16x8*)(Gs + tN<N>(pt * 16 + L16, 32 * ks + 8 * grp));
 #pragma unroll
         for (int s = 0; s < 2; ++s) acc[s][pt] = mfma16x16x32(a, Bop[s][ks], acc[s][pt]);
       }
     const float csL = css[Q - 1];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int j = J[s] * 16 + L16;
-      const float sc = fast_exp2(csL - css[j]);
-      float ts = 0.f;
+      const float sc = fast_exp2(csL - css[J[s] * 16 + L16]);
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
+      for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[s][pt][r] *= sc;
-        if (j < valid) {
-          const bf16x4 xv = *(const bf16x4*)(x + xrow0 + (int64_t)j * H * P + pt * 16 + 4 * grp);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ts += bf2f(xv[r]) * acc[s][pt][r];
-        }
-      }
-      ts += __shfl_xor(ts, 16, 64);
-      ts += __shfl_xor(ts, 32, 64);
-      if (grp == 0) tsv[j] = dts[j] * ts;
     }
     __syncthreads();  // g no longer needed: its space takes dY and x
 
     load_rows64<Q, NT>(Ys, dy + xrow0, (int64_t)H * P, valid);
     load_rows64<Q, NT>(Xs, x + xrow0, (int64_t)H * P, valid);
     __syncthreads();
+
+    // T^S_j from the state term alone (x rows are zero past the sequence end)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int j = J[s] * 16 + L16;
+      float ts = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const bf16x4 xv = *(const bf16x4*)(Xs + t64(j, pt * 16 + 4 * grp));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ts += bf2f(xv[r]) * acc[s][pt][r];
+      }
+      ts += __shfl_xor(ts, 16, 64);
+      ts += __shfl_xor(ts, 32, 64);
+      if (grp == 0) tsv[j] = dts[j] * ts;
+    }
 
     // ---- per triangle tile: masked, decayed C B^T to LDS (bfloat16) for the
     // dU products, and T = (M o CB) dt_j (dY x^T) for the rectangle sums:
@@ -293,8 +348,8 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
       f32x4 wv = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(Ys + (ti * 16 + L16) * 64 + 32 * kk + 8 * grp);
-        const bf16x8 bb = *(const bf16x8*)(Xs + (tj * 16 + L16) * 64 + 32 * kk + 8 * grp);
+        const bf16x8 a = *(const bf16x8*)(Ys + t64(ti * 16 + L16, 32 * kk + 8 * grp));
+        const bf16x8 bb = *(const bf16x8*)(Xs + t64(tj * 16 + L16, 32 * kk + 8 * grp));
         wv = mfma16x16x32(a, bb, wv);
       }
       const int j = tj * 16 + L16;
@@ -333,8 +388,8 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
         if (!live) bop = zero8();
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-          const bf16* yp = Ys + (32 * kp + 8 * grp + (L16 >> 2)) * 64 + pt * 16 + 4 * (L16 & 3);
-          const bf16x8 aop = cat(lds_read_tr(yp), lds_read_tr(yp + 4 * 64));
+          const int yr = 32 * kp + 8 * grp + (L16 >> 2), yc = pt * 16 + 4 * (L16 & 3);
+          const bf16x8 aop = cat(lds_read_tr(Ys + t64(yr, yc)), lds_read_tr(Ys + t64(yr + 4, yc)));
           acc[s][pt] = mfma16x16x32(aop, bop, acc[s][pt]);
         }
       }
@@ -354,8 +409,8 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
           const int p0 = pt * 16 + 4 * grp;
-          const bf16x4 xv = *(const bf16x4*)(x + off + p0);
-          const bf16x4 dv = *(const bf16x4*)(dy + off + p0);
+          const bf16x4 xv = *(const bf16x4*)(Xs + t64(j, p0));
+          const bf16x4 dv = *(const bf16x4*)(Ys + t64(j, p0));
           bf16x4 o;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -377,22 +432,17 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
 
     // ---- d(A dt)_k, ddt, and the dA and dD parts (one wave)
     if (w == 0) {
-      float dc = lane < wph ? dots[(((int64_t)b * H + h) * nc + c) * wph + lane] : 0.f;
-      dc = wave_sum(dc);
       constexpr int E = Q / 64;
-      const float* thh = th + (((int64_t)b * nc + c) * H + h) * nT * Q;
-      float rk[E], sh[E], ps[E];
+      const float dc = dcs[0];
+      float rk[E], ps[E], sh[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int k = lane * E + e;
         float v = 0.f;
         for (int i = 0; i < NW; ++i) v += rp[i * Q + k];
         rk[e] = v;
-        float t = 0.f;
-#pragma unroll
-        for (int nt = 0; nt < nT; ++nt) t += thh[nt * Q + k];
-        sh[e] = t;
         ps[e] = tsv[k];
+        sh[e] = ths[k];
       }
       // suffix sums of T^h (over i >= k) and exclusive prefix sums of T^S
       // (over j < k): inside the lane, then across lanes
@@ -444,15 +494,37 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
 // group's heads, written once as bfloat16 triangle tiles.  It does not depend
 // on the state size, so the dB/dC kernel's column tiles share it.
 // ---------------------------------------------------------------------------
+// Issues the direct-to-LDS loads of one head's dY and x rows of the chunk
+// ([Q][64] each, t64 chunk order; rows past the sequence end repeat its last
+// row and must be masked by the consumer) and its cs and dt rows.
+template <int Q>
+__device__ __forceinline__ void issue_rows_loads(uint32_t buf, const bf16* __restrict__ dyr,
+                                                 const bf16* __restrict__ xr, int64_t stride,
+                                                 int64_t valid, const float* __restrict__ cs,
+                                                 const float* __restrict__ dt) {
+  constexpr int NW = BwdCfg<Q>::NW, KT = Q / 8;  // wave-loads (1 KB) per tile
+  const int lane = lane_id();
+  for (int k = wave_id(); k < 2 * KT + 2; k += NW) {
+    if (k < 2 * KT) {
+      const int s = (k % KT) * 64 + lane;
+      int r = s >> 3;
+      const int ch = (s & 7) ^ ((r >> 1) & 7);
+      if (r > valid - 1) r = (int)(valid - 1);
+      dma16((k < KT ? dyr : xr) + (int64_t)r * stride + ch * 8, buf + k * 1024);
+    } else if (lane < Q / 4) {
+      dma16((k == 2 * KT ? cs : dt) + lane * 4, buf + 2 * Q * 128 + (k - 2 * KT) * Q * 4);
+    }
+  }
+}
+
 template <int Q>
 __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ dy, const float* __restrict__ dA_cs,
     const float* __restrict__ dt_T, bf16* __restrict__ wsum, int L, int H, int G, int nc) {
   using K = BwdCfg<Q>;
-  constexpr int P = 64, QT = K::QT, NT = K::NT, SLOTS = K::SLOTS;
-  __shared__ __attribute__((aligned(16))) bf16 Ys[Q * 64];
-  __shared__ __attribute__((aligned(16))) bf16 Xs[Q * 64];
-  __shared__ float css[Q], dts[Q];
+  constexpr int P = 64, QT = K::QT, SLOTS = K::SLOTS;
+  constexpr int BUF = 2 * Q * 128 + 2 * Q * 4;  // dY, x rows; cs, dt
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   int bid = blockIdx.x;
   const int g = bid % G;
@@ -464,31 +536,38 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
   const int w = wave_id();
   const int64_t tok0 = (int64_t)c * Q;
   const int64_t valid = (int64_t)L - tok0;
+  const uint32_t base = lds_addr(smem);
+
+  auto issue = [&](int h, int slot) {
+    const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;
+    const int64_t cb0 = (((int64_t)b * H + h) * nc + c) * Q;
+    issue_rows_loads<Q>(base + slot * BUF, dy + xrow0, x + xrow0, (int64_t)H * P, valid,
+                        dA_cs + cb0, dt_T + cb0);
+  };
 
   f32x4 ws[SLOTS];
 #pragma unroll
   for (int k = 0; k < SLOTS; ++k) ws[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  issue(g * HG, 0);
   for (int hh = 0; hh < HG; ++hh) {
-    const int h = g * HG + hh;
+    __builtin_amdgcn_s_waitcnt(0);  // this head's rows landed
+    __syncthreads();                // ... for every wave; the other buffer is free
+    if (hh + 1 < HG) issue(g * HG + hh + 1, (hh + 1) & 1);
+    const unsigned char* cur = smem + (hh & 1) * BUF;
+    const bf16* Ys = (const bf16*)cur;
+    const bf16* Xs = (const bf16*)(cur + Q * 128);
+    const float* css = (const float*)(cur + 2 * Q * 128);
+    const float* dts = css + Q;
     const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
-    const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;
-    load_rows64<Q, NT>(Ys, dy + xrow0, (int64_t)H * P, valid);
-    load_rows64<Q, NT>(Xs, x + xrow0, (int64_t)H * P, valid);
-    const int64_t cb0 = (((int64_t)b * H + h) * nc + c) * Q;
-    for (int i = threadIdx.x; i < Q; i += NT) {
-      css[i] = dA_cs[cb0 + i];
-      dts[i] = dt_T[cb0 + i];
-    }
-    __syncthreads();
 #pragma unroll
     for (int k = 0; k < SLOTS; ++k) {
       const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
       f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(Ys + (ti * 16 + L16) * 64 + 32 * kk + 8 * grp);
-        const bf16x8 bb = *(const bf16x8*)(Xs + (tj * 16 + L16) * 64 + 32 * kk + 8 * grp);
+        const bf16x8 a = *(const bf16x8*)(Ys + t64(ti * 16 + L16, 32 * kk + 8 * grp));
+        const bf16x8 bb = *(const bf16x8*)(Xs + t64(tj * 16 + L16, 32 * kk + 8 * grp));
         a4 = mfma16x16x32(a, bb, a4);
       }
       const int j = tj * 16 + L16;
@@ -497,11 +576,11 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
       for (int r = 0; r < 4; ++r) {
         const int i = ti * 16 + 4 * grp + r;
         const float e = fast_exp2(fminf(css[i] - csj, 0.f)) * dtj;
-        ws[k][r] += (i >= j ? e : 0.f) * a4[r];
+        // rows past the sequence end hold a repeated row: masked here
+        ws[k][r] += (i >= j && i < valid ? e : 0.f) * a4[r];
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
   }
 
   const int L16 = lane & 15, grp = lane >> 4;
@@ -517,8 +596,12 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
 // ---------------------------------------------------------------------------
 // chunk_bwd_dbdc
 // ---------------------------------------------------------------------------
-// Q/16 waves: wave w owns output row tile w of dB and dC (row tile w has w+1
-// causal tiles for dC and Q/16-w for dB: Q/16+1 in all, for every wave).
+// Q/16 waves: wave w owns output row tile w of dB and dC (row tile t has t+1
+// causal tiles for dC and Q/16-t for dB: Q/16+1 per tile, so every wave has
+// the same work).  Per head the wave's own rows of dY and x go straight to
+// registers in MFMA operand order, and the shared h and g column tiles, cs
+// and dt arrive by direct-to-LDS loads into a double buffer: the next head's
+// bytes are in flight while this head computes.
 template <int Q>
 struct BcCfg {
   static constexpr int QT = Q / 16, NW = QT, NT = 64 * NW;
@@ -526,18 +609,33 @@ struct BcCfg {
 
 template <int Q>
 struct BcLds {
-  using K = BwdCfg<Q>;
   static constexpr int BS = 0;                 // B columns [Q][64]
   static constexpr int CS = BS + Q * 128;      // C columns [Q][64]
-  static constexpr int HEAD = CS + Q * 128;    // per-head region
-  static constexpr int YS = HEAD;              // dY [Q][64]
-  static constexpr int XS = YS + Q * 128;      // x [Q][64]
-  static constexpr int HS = XS + Q * 128;      // h columns [64][64]
-  static constexpr int GS = HS + 8192;         // g columns [64][64]
-  static constexpr int CSS = GS + 8192;        // cs, dt [Q] each
-  static constexpr int BYTES = CSS + 2 * Q * 4;
-  static_assert(K::NTILE * 512 <= BYTES - HEAD, "summed W tiles fit in the per-head region");
+  static constexpr int BUF = 2 * 8192 + 2 * Q * 4;  // h, g columns [64][64]; cs, dt
+  static constexpr int HEAD = CS + Q * 128;    // two head buffers, later the summed W
+  static constexpr int WT = BwdCfg<Q>::NTILE * 512;
+  static constexpr int BYTES = HEAD + (WT > 2 * BUF ? WT : 2 * BUF);
 };
+
+// Issues the direct-to-LDS loads of one head's h and g column tiles (64 rows
+// x 64 columns, stored with the t64 chunk order) and its cs and dt rows.
+template <int Q>
+__device__ __forceinline__ void issue_head_loads(uint32_t buf, const bf16* __restrict__ hsrc,
+                                                 const bf16* __restrict__ gsrc, int N,
+                                                 const float* __restrict__ cs,
+                                                 const float* __restrict__ dt) {
+  constexpr int NW = BcCfg<Q>::NW;
+  const int lane = lane_id();
+  for (int k = wave_id(); k < 18; k += NW) {
+    if (k < 16) {
+      const int s = (k & 7) * 64 + lane;  // chunk at LDS position s of the tile
+      const int r = s >> 3, ch = (s & 7) ^ ((r >> 1) & 7);
+      dma16((k < 8 ? hsrc : gsrc) + (int64_t)r * N + ch * 8, buf + (k >> 3) * 8192 + (k & 7) * 1024);
+    } else if (lane < Q / 4) {
+      dma16((k == 16 ? cs : dt) + lane * 4, buf + 16384 + (k - 16) * Q * 4);
+    }
+  }
+}
 
 template <int Q>
 __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
@@ -566,19 +664,40 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
 
   const int lane = lane_id();
   const int w = wave_id();
+  const int L16 = lane & 15, grp = lane >> 4;
   const int64_t tok0 = (int64_t)c * Q;
   const int64_t valid = (int64_t)L - tok0;
   const int R = w;  // output row tile
+  const int row = R * 16 + L16;  // this lane's operand row
 
   bf16* Bs = (bf16*)(smem + S::BS);
   bf16* Cs = (bf16*)(smem + S::CS);
-  bf16* Ys = (bf16*)(smem + S::YS);
-  bf16* Xs = (bf16*)(smem + S::XS);
-  bf16* Hs = (bf16*)(smem + S::HS);
-  bf16* Gs = (bf16*)(smem + S::GS);
-  float* css = (float*)(smem + S::CSS);
-  float* dts = css + Q;
+  const uint32_t head_lds = lds_addr(smem + S::HEAD);
 
+  auto st_of = [&](int h) {
+    return (((int64_t)b * nc + c) * H + h) * (int64_t)P * N + nt * 64;
+  };
+  auto cs_of = [&](int h) { return (((int64_t)b * H + h) * nc + c) * (int64_t)Q; };
+  // this lane's dY and x operand pieces of head h (zero past the sequence end)
+  auto load_rows = [&](int h, bf16x8 (&ay)[2], bf16x8 (&ax)[2]) {
+    const int rw = opaque(row);
+    const int64_t off = (((int64_t)b * L + tok0 + rw) * H + h) * P + 8 * opaque(grp);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      ay[kk] = zero8();
+      ax[kk] = zero8();
+      if (row < valid) {
+        ay[kk] = *(const bf16x8*)(dy + off + 32 * kk);
+        ax[kk] = *(const bf16x8*)(x + off + 32 * kk);
+      }
+    }
+  };
+
+  const int h0 = g * HG;
+  issue_head_loads<Q>(head_lds, hst + st_of(h0), gst + st_of(h0), N, dA_cs + cs_of(h0),
+                      dt_T + cs_of(h0));
+  bf16x8 nY[2], nX[2];
+  load_rows(h0, nY, nX);
   {
     const int64_t row0 = ((int64_t)b * L + tok0) * G + g;
     load_rows64<Q, NT>(Bs, Bm + row0 * N + nt * 64, (int64_t)G * N, valid);
@@ -593,75 +712,68 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
   }
 
   for (int hh = 0; hh < HG; ++hh) {
-    const int h = g * HG + hh;
-    const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
-    const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;
-    load_rows64<Q, NT>(Ys, dy + xrow0, (int64_t)H * P, valid);
-    load_rows64<Q, NT>(Xs, x + xrow0, (int64_t)H * P, valid);
-    const int64_t st0 = (((int64_t)b * nc + c) * H + h) * (int64_t)P * N + nt * 64;
-    load_rows64<64, NT>(Hs, hst + st0, N, 64);
-    load_rows64<64, NT>(Gs, gst + st0, N, 64);
-    const int64_t cb0 = (((int64_t)b * H + h) * nc + c) * Q;
-    for (int i = threadIdx.x; i < Q; i += NT) {
-      css[i] = dA_cs[cb0 + i];
-      dts[i] = dt_T[cb0 + i];
-    }
+    const int h = h0 + hh;
+    // this head's buffer has landed (and every wave is done with the other one)
+    __builtin_amdgcn_s_waitcnt(0);  // every load of this wave, direct-to-LDS ones included
     __syncthreads();
+    const unsigned char* cur = smem + S::HEAD + (hh & 1) * S::BUF;
+    const bf16* Hs = (const bf16*)cur;
+    const bf16* Gs = (const bf16*)(cur + 8192);
+    const float* css = (const float*)(cur + 16384);
+    const float* dts = css + Q;
+    const bf16x8 aY[2] = {nY[0], nY[1]}, aX[2] = {nX[0], nX[1]};
+    if (hh + 1 < HG) {
+      issue_head_loads<Q>(head_lds + ((hh + 1) & 1) * S::BUF, hst + st_of(h + 1),
+                          gst + st_of(h + 1), N, dA_cs + cs_of(h + 1), dt_T + cs_of(h + 1));
+      load_rows(h + 1, nY, nX);
+    }
 
     // state terms of this wave's rows: 2^cs_i (dY h)[i, n] into dC and
     // 2^(cs_last - cs_j) dt_j (X g)[j, n] into dB; T^h_i parts
-    {
-      const float csL = css[Q - 1];
-      bf16x8 aY[2], aX[2];
+    const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
+    const float csL = css[Q - 1];
+    float eC[4], eB[4], thr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = R * 16 + 4 * grp + r;
+      eC[r] = fast_exp2(css[i]);
+      eB[r] = fast_exp2(csL - css[i]) * dts[i];
+      thr[r] = 0.f;
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      f32x4 tc = f32x4{0.f, 0.f, 0.f, 0.f}, tb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        aY[kk] = *(const bf16x8*)(Ys + (R * 16 + L16) * 64 + 32 * kk + 8 * grp);
-        aX[kk] = *(const bf16x8*)(Xs + (R * 16 + L16) * 64 + 32 * kk + 8 * grp);
+        const int r0 = 32 * kk + 8 * grp + (L16 >> 2), c0 = ct * 16 + 4 * (L16 & 3);
+        const int oa = t64(r0, c0), ob = t64(r0 + 4, c0);
+        const bf16x8 hb = cat(lds_read_tr(Hs + oa), lds_read_tr(Hs + ob));
+        const bf16x8 gb = cat(lds_read_tr(Gs + oa), lds_read_tr(Gs + ob));
+        tc = mfma16x16x32(aY[kk], hb, tc);
+        tb = mfma16x16x32(aX[kk], gb, tb);
       }
-      float eC[4], eB[4], thr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = R * 16 + 4 * grp + r;
-        eC[r] = fast_exp2(css[i]);
-        eB[r] = fast_exp2(csL - css[i]) * dts[i];
-        thr[r] = 0.f;
-      }
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        f32x4 tc = f32x4{0.f, 0.f, 0.f, 0.f}, tb = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int ro = (32 * kk + 8 * grp + (L16 >> 2)) * 64 + ct * 16 + 4 * (L16 & 3);
-          const bf16x8 hb = cat(lds_read_tr(Hs + ro), lds_read_tr(Hs + ro + 4 * 64));
-          const bf16x8 gb = cat(lds_read_tr(Gs + ro), lds_read_tr(Gs + ro + 4 * 64));
-          tc = mfma16x16x32(aY[kk], hb, tc);
-          tb = mfma16x16x32(aX[kk], gb, tb);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float vc = eC[r] * tc[r];
-          accC[ct][r] += vc;
-          accB[ct][r] += eB[r] * tb[r];
-          thr[r] += vc * bf2f(Cs[(R * 16 + 4 * grp + r) * 64 + ct * 16 + L16]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // T^h parts of this column tile: 2^cs_i dy_i . (h C_i) over its 64 columns
-      float* tho = th + ((((int64_t)b * nc + c) * H + h) * nT + nt) * Q + R * 16 + 4 * grp;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = thr[r];
-#pragma unroll
-        for (int mm = 1; mm < 16; mm <<= 1) v += __shfl_xor(v, mm, 64);
-        if (L16 == 0) tho[r] = v;
+        const float vc = eC[r] * tc[r];
+        accC[ct][r] += vc;
+        accB[ct][r] += eB[r] * tb[r];
+        thr[r] += vc * bf2f(Cs[t64(R * 16 + 4 * grp + r, ct * 16 + L16)]);
       }
     }
-    __syncthreads();
+    // T^h parts of this column tile: 2^cs_i dy_i . (h C_i) over its 64 columns
+    float* tho = th + ((((int64_t)b * nc + c) * H + h) * nT + nt) * Q + R * 16 + 4 * grp;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = thr[r];
+#pragma unroll
+      for (int mm = 1; mm < 16; mm <<= 1) v += __shfl_xor(v, mm, 64);
+      if (L16 == 0) tho[r] = v;
+    }
   }
 
-  const int L16 = lane & 15, grp = lane >> 4;
   // the group's summed W (bfloat16 triangle tiles) into LDS, then the
   // products with B and C
+  __syncthreads();
   bf16* Wt = (bf16*)(smem + S::HEAD);
   {
     const bf16* src = wsum + m * (int64_t)(BwdCfg<Q>::NTILE * 256);
@@ -680,8 +792,8 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
       if (!live) a = zero8();
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const bf16* bp = Bs + (32 * kp + 8 * grp + (L16 >> 2)) * 64 + ct * 16 + 4 * (L16 & 3);
-        const bf16x8 bb = cat(lds_read_tr(bp), lds_read_tr(bp + 4 * 64));
+        const int br = 32 * kp + 8 * grp + (L16 >> 2), bcol = ct * 16 + 4 * (L16 & 3);
+        const bf16x8 bb = cat(lds_read_tr(Bs + t64(br, bcol)), lds_read_tr(Bs + t64(br + 4, bcol)));
         accC[ct] = mfma16x16x32(a, bb, accC[ct]);
       }
     }
@@ -695,8 +807,8 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
       if (!live) a = zero8();
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const bf16* cp = Cs + (32 * kp + 8 * grp + (L16 >> 2)) * 64 + ct * 16 + 4 * (L16 & 3);
-        const bf16x8 cc = cat(lds_read_tr(cp), lds_read_tr(cp + 4 * 64));
+        const int cr = 32 * kp + 8 * grp + (L16 >> 2), ccol = ct * 16 + 4 * (L16 & 3);
+        const bf16x8 cc = cat(lds_read_tr(Cs + t64(cr, ccol)), lds_read_tr(Cs + t64(cr + 4, ccol)));
         accB[ct] = mfma16x16x32(a, cc, accB[ct]);
       }
     }
@@ -776,7 +888,12 @@ template <int Q>
 hipError_t launch_dbdc(const Dims& d, const void* x, const void* dy, const void* B, const void* C,
                        const float* dA_cs, const float* dt_T, const void* hst, const void* gst,
                        void* wsum, void* dB, void* dC, float* th, hipStream_t s) {
-  chunk_bwd_wsum_kernel<Q><<<(unsigned)(d.B * d.nc * d.G), BwdCfg<Q>::NT, 0, s>>>(
+  auto wk = chunk_bwd_wsum_kernel<Q>;
+  constexpr int wlds = 2 * (2 * Q * 128 + 2 * Q * 4);
+  static const hipError_t wattr =
+      hipFuncSetAttribute((const void*)wk, hipFuncAttributeMaxDynamicSharedMemorySize, wlds);
+  if (wattr != hipSuccess) return wattr;
+  wk<<<(unsigned)(d.B * d.nc * d.G), BwdCfg<Q>::NT, wlds, s>>>(
       (const bf16*)x, (const bf16*)dy, dA_cs, dt_T, (bf16*)wsum, (int)d.L, (int)d.H, (int)d.G,
       (int)d.nc);
   const hipError_t e = hipGetLastError();
