@@ -202,7 +202,7 @@ int check_forward_args(const mamba2_dims* dims, m2::Dims* d, const void* x, cons
 // and boundary dot-product parts, the groups' summed interaction matrices,
 // per-chunk dA and dD parts).
 struct BwdWorkspace {
-  size_t cs, st, hst, fin, th, wsum, dots, part, total;
+  size_t cs, st, hst, fin, th, wsum, rsum, dots, part, total;
   int64_t wph;
 };
 
@@ -215,9 +215,10 @@ BwdWorkspace plan_backward(const m2::Dims& d) {
   w.fin = round256((size_t)(d.B * d.H * d.P * d.N) * sizeof(float));
   w.th = round256((size_t)(d.B * d.nc * d.H * (d.N / 64) * d.Q) * sizeof(float));
   w.wsum = round256((size_t)(d.B * d.nc * d.G) * (size_t)(d.Q * (d.Q + 16) / 2) * 2);
+  w.rsum = w.cs;
   w.dots = round256((size_t)(d.B * d.H * d.nc * w.wph) * sizeof(float));
   w.part = round256((size_t)(d.B * d.nc * d.H) * sizeof(float));
-  w.total = 2 * w.cs + w.st + 2 * w.hst + w.fin + w.th + w.wsum + w.dots + 2 * w.part;
+  w.total = 2 * w.cs + w.st + 2 * w.hst + w.fin + w.th + w.wsum + w.rsum + w.dots + 2 * w.part;
   return w;
 }
 
@@ -246,6 +247,8 @@ int enqueue_backward(const m2::Dims& d, const void* x, const void* dt, const flo
   p += w.th;
   void* wsum = p;
   p += w.wsum;
+  float* rsum = (float*)p;
+  p += w.rsum;
   float* dots = (float*)p;
   p += w.dots;
   float* dA_part = (float*)p;
@@ -271,11 +274,13 @@ int enqueue_backward(const m2::Dims& d, const void* x, const void* dt, const flo
           : e;
   mark();
   e = e == hipSuccess
-          ? m2::launch_chunk_bwd_dbdc(d, x, dy, B, C, dA_cs, dt_T, hst, gst, wsum, dB, dC, th, s)
+          ? m2::launch_chunk_bwd_dbdc(d, x, dy, B, C, dA_cs, dt_T, hst, gst, wsum, rsum, dB, dC,
+                                      th, s)
           : e;
   mark();
   e = e == hipSuccess ? m2::launch_chunk_bwd_dx(d, x, dy, B, C, dA_cs, dt_T, gst, dots,
-                                                (int)w.wph, th, A, D, dx, ddt, dA_part, dD_part, s)
+                                                (int)w.wph, th, rsum, A, D, dx, ddt, dA_part,
+                                                dD_part, s)
                       : e;
   mark();
   e = e == hipSuccess ? m2::launch_bwd_param_sums(d, dA_part, dD_part, dA, D ? dD : nullptr, s)

@@ -126,20 +126,6 @@ __device__ __forceinline__ void load_rows64(bf16* dst, const bf16* __restrict__ 
 // ---------------------------------------------------------------------------
 // chunk_bwd_dx
 // ---------------------------------------------------------------------------
-template <int Q, int N>
-struct DxLds {
-  using K = BwdCfg<Q>;
-  // g [64][N] for the state term, then dY and x rows [Q][64] each
-  static constexpr int R1 = (64 * N * 2 > Q * 256) ? 64 * N * 2 : Q * 256;
-  static constexpr int GS = 0, YS = 0, XS = Q * 128;
-  static constexpr int GT = R1;                        // masked C B^T tiles, bf16
-  static constexpr int CSS = GT + K::NTILE * 512;      // cs, dt, x.dU, T^S, T^h [Q] each
-  static constexpr int RP = CSS + 5 * Q * 4 + 16;      // per-wave rectangle-sum parts
-  static constexpr int RED = RP + K::NW * Q * 4;       // per-wave dy.x parts
-  static constexpr int BYTES = RED + 64;
-  static_assert(2 * Q * 128 <= BYTES, "setup slices fit in the same space");
-};
-
 // v + (v of the lane CTRL selects inside its 16-lane row), 0 where none.
 template <int CTRL>
 __device__ __forceinline__ float row_shr_add(float v) {
@@ -159,25 +145,100 @@ __device__ __forceinline__ float row_prev(float v) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false));
 }
 
+typedef short s16x4v __attribute__((ext_vector_type(4)));
+
+// D(16x16, f32) += A(16x16, bf16) * B(16x16, bf16): lane l holds A row (l & 15)
+// and B column (l & 15) at K = 4 (l >> 4) .. +3, the accumulator as for the
+// 16x16x32 form.  Its K layout is the accumulator's row layout, so a float32
+// tile feeds it as a B operand straight from registers.
+__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4v, a),
+                                                   __builtin_bit_cast(s16x4v, b), c, 0, 0, 0);
+}
+
+// Slot k of wave w in chunk_bwd_dx: the column strips of tiles w and
+// QT-1-w, (w..QT-1, w) then (QT-1-w..QT-1, QT-1-w): QT+1 tiles for every wave.
+template <int QT>
+__device__ __forceinline__ int cslot_strip(int w, int k) { return k < QT - w ? 0 : 1; }
+template <int QT>
+__device__ __forceinline__ int cslot_ti(int w, int k) {
+  return k < QT - w ? w + k : (QT - 1 - w) + (k - (QT - w));
+}
+template <int QT>
+__device__ __forceinline__ int cslot_tj(int w, int k) { return k < QT - w ? w : QT - 1 - w; }
+
+template <int Q, int N>
+struct DxLds {
+  using K = BwdCfg<Q>;
+  static constexpr int nT = N / 64;
+  // one head's buffer: g [64][N] (tN order), dY [Q][64] (t64 order), cs, dt,
+  // T^h parts [nT][Q], rectangle sums R [Q], boundary dot parts [64]
+  static constexpr int GS = 0, YS = 64 * N * 2, CS = YS + Q * 128, DT = CS + Q * 4;
+  static constexpr int TH = DT + Q * 4, RS = TH + nT * Q * 4, DOT = RS + Q * 4;
+  static constexpr int BUF = DOT + 64 * 4;
+  static constexpr int SM = 2 * BUF;                  // x.dU, T^S [Q] each
+  static constexpr int RED = SM + 2 * Q * 4;          // per-wave dy.x parts
+  static constexpr int BYTES = RED + 64;
+  static_assert(2 * Q * 128 <= 2 * BUF, "setup slices of C and B fit in the head buffers");
+};
+
+// Issues the direct-to-LDS loads of one head's buffer.
+template <int Q, int N>
+__device__ __forceinline__ void issue_dx_loads(uint32_t buf, const bf16* __restrict__ gsrc,
+                                               const bf16* __restrict__ dyr, int64_t stride,
+                                               int64_t valid, const float* __restrict__ cs,
+                                               const float* __restrict__ dt,
+                                               const float* __restrict__ thp,
+                                               const float* __restrict__ rs,
+                                               const float* __restrict__ dp, int wph) {
+  using S = DxLds<Q, N>;
+  constexpr int TH4 = S::nT * Q / 4;  // 16-byte pieces of the T^h parts
+  constexpr int NW = BwdCfg<Q>::NW, KG = N / 8, KY = Q / 8, KTH = (TH4 + 63) / 64;
+  constexpr int KTOT = KG + KY + KTH + 4;
+  const int lane = lane_id();
+  for (int k = wave_id(); k < KTOT; k += NW) {
+    if (k < KG) {  // g rows: N/8 chunks each
+      const int s = k * 64 + lane;
+      const int r = s / (N / 8), pos = s % (N / 8);
+      const int ch = (N >= 128) ? (pos ^ (r & 15)) : (pos ^ ((r >> 1) & 7));
+      dma16(gsrc + (int64_t)r * N + ch * 8, buf + S::GS + k * 1024);
+    } else if (k < KG + KY) {  // dY rows (past the sequence end: the last row again)
+      const int s = (k - KG) * 64 + lane;
+      int r = s >> 3;
+      const int ch = (s & 7) ^ ((r >> 1) & 7);
+      if (r > valid - 1) r = (int)(valid - 1);
+      dma16(dyr + (int64_t)r * stride + ch * 8, buf + S::YS + (k - KG) * 1024);
+    } else if (k < KG + KY + KTH) {
+      const int kk = k - KG - KY;
+      if (kk * 64 + lane < TH4) dma16(thp + (kk * 64 + lane) * 4, buf + S::TH + kk * 1024);
+    } else {
+      const int kk = k - KG - KY - KTH;  // 0: cs, 1: dt, 2: R, 3: dot parts
+      const int n4 = kk == 3 ? wph / 4 : Q / 4;
+      const float* src = kk == 0 ? cs : kk == 1 ? dt : kk == 2 ? rs : dp;
+      const int off = kk == 0 ? S::CS : kk == 1 ? S::DT : kk == 2 ? S::RS : S::DOT;
+      if (lane < n4) dma16(src + lane * 4, buf + off + lane * 16);
+    }
+  }
+}
+
 // The log-decay gradient is formed without cancellation: for position k,
-//   d(A dt)_k = sum_{i >= k > j} T_ij + sum_{i >= k} T^h_i + sum_{j < k} T^S_j
-//               + 2^cs_last <g, h_start>,
-// T_ij = (M o CB)_ij dt_j (dy_i . x_j) for i > j (the in-chunk terms whose
-// decay spans position k), T^h_i = 2^cs_i dy_i . (h_start C_i) (from the
-// dB/dC kernel), T^S_j = dt_j x_j . dU^state_j.  Every sum is of terms of
-// one interaction each, so no large opposite contributions cancel.
+//   d(A dt)_k = R_k + sum_{i >= k} T^h_i + sum_{j < k} T^S_j + 2^cs_last <g, h_start>,
+// R_k = sum_{i >= k > j} (M o CB)_ij dt_j (dy_i . x_j) (from the summed-W
+// kernel), T^h_i = 2^cs_i dy_i . (h_start C_i) (from the dB/dC kernel) and
+// T^S_j = dt_j x_j . dU^state_j (here).  Every sum is of terms of single
+// interactions, so no large opposite contributions cancel.
 template <int Q, int N>
 __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ dy, const bf16* __restrict__ Bm,
     const bf16* __restrict__ Cm, const float* __restrict__ dA_cs, const float* __restrict__ dt_T,
     const bf16* __restrict__ gst, const float* __restrict__ dots, const float* __restrict__ th,
-    const float* __restrict__ A, const float* __restrict__ D, bf16* __restrict__ dx,
-    bf16* __restrict__ ddt, float* __restrict__ dA_part, float* __restrict__ dD_part, int L, int H,
-    int G, int nc, int hpw, int slices, int wph) {
+    const float* __restrict__ rsum, const float* __restrict__ A, const float* __restrict__ D,
+    bf16* __restrict__ dx, bf16* __restrict__ ddt, float* __restrict__ dA_part,
+    float* __restrict__ dD_part, int L, int H, int G, int nc, int hpw, int slices, int wph) {
   using K = BwdCfg<Q>;
   using S = DxLds<Q, N>;
   constexpr int P = 64, QT = K::QT, NW = K::NW, NT = K::NT, SLOTS = K::SLOTS, KN = N / 32;
-  constexpr int nT = N / 64;
+  constexpr int nT = S::nT;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   int bid = blockIdx.x;
@@ -192,14 +253,14 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
   const int nh = min(hpw, HG - slice * hpw);
   if (nh <= 0) return;  // whole workgroup
 
-  const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = wave_id();
   const int64_t tok0 = (int64_t)c * Q;
   const int64_t valid = (int64_t)L - tok0;  // rows of this chunk inside the sequence
   const int J[2] = {w, QT - 1 - w};
+  const uint32_t base = lds_addr(smem);
 
-  // ---- C B^T of the group (float32, this wave's triangle tiles) and the
+  // ---- C B^T of the group (float32, this wave's column strips) and the
   // B operands of this wave's output columns for the state term.
   f32x4 cb[SLOTS];
 #pragma unroll
@@ -218,7 +279,7 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
       __syncthreads();
 #pragma unroll
       for (int k = 0; k < SLOTS; ++k) {
-        const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
+        const int ti = cslot_ti<QT>(w, k), tj = cslot_tj<QT>(w, k);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const bf16x8 a = *(const bf16x8*)(Cs + t64(ti * 16 + L16, 32 * kk + 8 * grp));
@@ -233,175 +294,114 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
         for (int kk = 0; kk < 2; ++kk)
           Bop[s][2 * ns + kk] = *(const bf16x8*)(Bs + t64(J[s] * 16 + L16, 32 * kk + 8 * grp));
     }
-    __syncthreads();
+    __syncthreads();  // slices consumed before the head buffers take their space
   }
 
-  bf16* Gs = (bf16*)(smem + S::GS);
-  bf16* Ys = (bf16*)(smem + S::YS);
-  bf16* Xs = (bf16*)(smem + S::XS);
-  bf16* Gt = (bf16*)(smem + S::GT);
-  float* css = (float*)(smem + S::CSS);
-  float* dts = css + Q;
-  float* exs = dts + Q;
+  auto issue = [&](int h, int slot) {
+    const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;
+    const int64_t cb0 = (((int64_t)b * H + h) * nc + c) * Q;
+    issue_dx_loads<Q, N>(base + slot * S::BUF,
+                         gst + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N, dy + xrow0,
+                         (int64_t)H * P, valid, dA_cs + cb0, dt_T + cb0,
+                         th + (((int64_t)b * nc + c) * H + h) * nT * Q, rsum + cb0,
+                         dots + (((int64_t)b * H + h) * nc + c) * wph, wph);
+  };
+
+  float* exs = (float*)(smem + S::SM);
   float* tsv = exs + Q;
-  float* ths = tsv + Q;
-  float* dcs = ths + Q;  // one value: 2^cs_last <g, h_start>
-  float* rp = (float*)(smem + S::RP);
   float* red = (float*)(smem + S::RED);
 
-  for (int hh = 0; hh < nh; ++hh) {
-    const int h = h0 + hh;
+  // this lane's x values of head h in the accumulator layout (zero past the
+  // end); loaded one head ahead, so that no wait inside a head's work would
+  // also wait for the next head's direct-to-LDS loads
+  bf16x4 xr[2][4];
+  auto load_x = [&](int h) {
     const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
-    const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;  // x, dy row tok0
-    {
-      const bf16* src = gst + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
-      constexpr int IT = P * N / 8 / NT;
-      static_assert(P * N / 8 % NT == 0, "g tile splits evenly over the threads");
-      bf16x8 v[IT];
-#pragma unroll
-      for (int it = 0; it < IT; ++it) v[it] = *(const bf16x8*)(src + (tid + it * NT) * 8);
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int s = tid + it * NT;
-        *(bf16x8*)(Gs + tN<N>(s / (N / 8), (s % (N / 8)) * 8)) = v[it];
-      }
-    }
-    const int64_t cb0 = (((int64_t)b * H + h) * nc + c) * Q;
-    for (int i = tid; i < Q; i += NT) {
-      css[i] = dA_cs[cb0 + i];
-      dts[i] = dt_T[cb0 + i];
-    }
-    for (int i = tid; i < NW * Q; i += NT) rp[i] = 0.f;
-    {
-      const float* thh = th + (((int64_t)b * nc + c) * H + h) * nT * Q;
-      for (int i = tid; i < Q; i += NT) {
-        float t = 0.f;
-#pragma unroll
-        for (int nt = 0; nt < nT; ++nt) t += thh[nt * Q + i];
-        ths[i] = t;
-      }
-      if (w == NW - 1) {
-        float dc = lane < wph ? dots[(((int64_t)b * H + h) * nc + c) * wph + lane] : 0.f;
-        dc = wave_sum(dc);
-        if (lane == 0) dcs[0] = dc;
-      }
-    }
-    __syncthreads();
-
-    // ---- dU^T[p][j] state term for this wave's column tiles, scaled per
-    // column by 2^(cs_last - cs_j); T^S_j = dt_j x_j . dU^state_j
-    f32x4 acc[2][4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[s][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KN; ++ks)
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const bf16x8 a = *(const bf16x8*)(Gs + tN<N>(pt * 16 + L16, 32 * ks + 8 * grp));
-#pragma unroll
-        for (int s = 0; s < 2; ++s) acc[s][pt] = mfma16x16x32(a, Bop[s][ks], acc[s][pt]);
-      }
-    const float csL = css[Q - 1];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const float sc = fast_exp2(csL - css[J[s] * 16 + L16]);
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[s][pt][r] *= sc;
-    }
-    __syncthreads();  // g no longer needed: its space takes dY and x
-
-    load_rows64<Q, NT>(Ys, dy + xrow0, (int64_t)H * P, valid);
-    load_rows64<Q, NT>(Xs, x + xrow0, (int64_t)H * P, valid);
-    __syncthreads();
-
-    // T^S_j from the state term alone (x rows are zero past the sequence end)
+    const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int j = J[s] * 16 + L16;
-      float ts = 0.f;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const bf16x4 xv = *(const bf16x4*)(Xs + t64(j, pt * 16 + 4 * grp));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ts += bf2f(xv[r]) * acc[s][pt][r];
-      }
-      ts += __shfl_xor(ts, 16, 64);
-      ts += __shfl_xor(ts, 32, 64);
-      if (grp == 0) tsv[j] = dts[j] * ts;
-    }
-
-    // ---- per triangle tile: masked, decayed C B^T to LDS (bfloat16) for the
-    // dU products, and T = (M o CB) dt_j (dY x^T) for the rectangle sums:
-    // row prefix sums along each row strip, column sums of those prefixes
-    float carry[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < SLOTS; ++k) {
-      const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
-      if (k == w + 1) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) carry[r] = 0.f;
-      }
-      f32x4 wv = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(Ys + t64(ti * 16 + L16, 32 * kk + 8 * grp));
-        const bf16x8 bb = *(const bf16x8*)(Xs + t64(tj * 16 + L16, 32 * kk + 8 * grp));
-        wv = mfma16x16x32(a, bb, wv);
-      }
-      const int j = tj * 16 + L16;
-      const float csj = css[j], dtj = dts[j];
-      bf16* dst = Gt + tix_of(ti, tj) * 256 + 4 * grp * 16 + L16;
-      float col = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = ti * 16 + 4 * grp + r;
-        const float e = fast_exp2(fminf(css[i] - csj, 0.f));
-        const float gm = (i >= j) ? cb[k][r] * e : 0.f;
-        dst[r * 16] = f2bf(gm);
-        const float t = (i > j) ? gm * dtj * wv[r] : 0.f;
-        const float inc = row_scan16(t);
-        const float pm = carry[r] + row_prev(inc);  // sum_{j' < j} T[i][j'] over the row
-        carry[r] += __shfl(inc, 15, 16);
-        if (j <= i) col += pm;
-      }
-      col += __shfl_xor(col, 16, 64);
-      col += __shfl_xor(col, 32, 64);
-      if (grp == 0) rp[w * Q + j] += col;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-
-    // ---- causal part of dU^T
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int Js = J[s];
-      for (int kp = Js >> 1; kp < QT / 2; ++kp) {
-        const int ti = 2 * kp + (grp >> 1);
-        const bool live = ti >= Js;
-        const int tic = live ? ti : Js;
-        const bf16* gp = Gt + tix_of(tic, Js) * 256 + (8 * (grp & 1) + (L16 >> 2)) * 16 + 4 * (L16 & 3);
-        bf16x8 bop = cat(lds_read_tr(gp), lds_read_tr(gp + 64));
-        if (!live) bop = zero8();
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          const int yr = 32 * kp + 8 * grp + (L16 >> 2), yc = pt * 16 + 4 * (L16 & 3);
-          const bf16x8 aop = cat(lds_read_tr(Ys + t64(yr, yc)), lds_read_tr(Ys + t64(yr + 4, yc)));
-          acc[s][pt] = mfma16x16x32(aop, bop, acc[s][pt]);
-        }
+        xr[s][pt] = __builtin_bit_cast(bf16x4, (short __attribute__((ext_vector_type(4)))){0, 0, 0, 0});
+        if (j < valid)
+          xr[s][pt] = *(const bf16x4*)(x + xrow0 + (int64_t)j * H * P + pt * 16 + 4 * grp);
       }
     }
+  };
 
-    // ---- epilogue: acc[s][pt][r] = dU[j = 16 J[s] + L16][p = 16 pt + 4 grp + r]
-    const float Ah = A[h];
+  issue(h0, 0);
+  load_x(h0);
+  for (int hh = 0; hh < nh; ++hh) {
+    const int h = h0 + hh;
+    __builtin_amdgcn_s_waitcnt(0);  // this head's buffer and x values landed
+    __syncthreads();                // ... for every wave; the other buffer is free
+    if (hh + 1 < nh) issue(h + 1, (hh + 1) & 1);
+    const unsigned char* cur = smem + (hh & 1) * S::BUF;
+    const bf16* Gs = (const bf16*)(cur + S::GS);
+    const bf16* Ys = (const bf16*)(cur + S::YS);
+    const float* css = (const float*)(cur + S::CS);
+    const float* dts = (const float*)(cur + S::DT);
+    const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
+    const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;
+
+    // One pass per output column tile s (tiles w and QT-1-w): the state
+    // term of dU^T[p][j], scaled per column by 2^(cs_last - cs_j), T^S_j,
+    // the causal part sum_{i >= j} dY^T[p][i] (M o CB)[i][j] with the masked,
+    // decayed C B^T tile of each slot of the strip used as the B operand from
+    // registers (16x16x16: its K rows are the accumulator's rows), and the
+    // epilogue.  acc[pt][r] = dU[j = 16 J[s] + L16][p = 16 pt + 4 grp + r].
+    const float csL = css[Q - 1];
     const float Dh = D ? D[h] : 0.f;
     float dd = 0.f;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int j = J[s] * 16 + L16;
+      f32x4 acc[4];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KN; ++ks) {
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          const bf16x8 a = *(const bf16x8*)(Gs + tN<N>(pt * 16 + L16, 32 * ks + 8 * grp));
+          acc[pt] = mfma16x16x32(a, Bop[s][ks], acc[pt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const float sc = fast_exp2(csL - css[j]);
+      float ts = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[pt][r] *= sc;
+          ts += bf2f(xr[s][pt][r]) * acc[pt][r];
+        }
+      ts += __shfl_xor(ts, 16, 64);
+      ts += __shfl_xor(ts, 32, 64);
+      if (grp == 0) tsv[j] = dts[j] * ts;  // T^S_j
+
+#pragma unroll
+      for (int k = 0; k < SLOTS; ++k) {
+        if (cslot_strip<QT>(w, k) == s) {
+          const int ti = cslot_ti<QT>(w, k);
+          const float csj = css[j];
+          bf16x4 bop;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = ti * 16 + 4 * grp + r;
+            const float e = fast_exp2(fminf(css[i] - csj, 0.f));
+            bop[r] = f2bf(i >= j ? cb[k][r] * e : 0.f);
+          }
+          const int yr = ti * 16 + 4 * grp + (L16 >> 2);
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt)
+            acc[pt] = mfma16x16x16(lds_read_tr(Ys + t64(yr, pt * 16 + 4 * (L16 & 3))), bop, acc[pt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
       float ex = 0.f;
       if (j < valid) {
         const float dtj = dts[j];
@@ -409,12 +409,11 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
           const int p0 = pt * 16 + 4 * grp;
-          const bf16x4 xv = *(const bf16x4*)(Xs + t64(j, p0));
           const bf16x4 dv = *(const bf16x4*)(Ys + t64(j, p0));
           bf16x4 o;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float du = acc[s][pt][r], xf = bf2f(xv[r]), df = bf2f(dv[r]);
+            const float du = acc[pt][r], xf = bf2f(xr[s][pt][r]), df = bf2f(dv[r]);
             o[r] = f2bf(dtj * du + Dh * df);
             ex += xf * du;
             dd += df * xf;
@@ -426,23 +425,29 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
       ex += __shfl_xor(ex, 32, 64);
       if (grp == 0) exs[j] = ex;
     }
+    const float Ah = A[h];
     dd = wave_sum(dd);
     if (lane == 0) red[w] = dd;
-    __syncthreads();
+    if (hh + 1 < nh) load_x(h + 1);
+    lds_barrier();  // LDS only: the loads in flight keep flying
 
     // ---- d(A dt)_k, ddt, and the dA and dD parts (one wave)
     if (w == 0) {
       constexpr int E = Q / 64;
-      const float dc = dcs[0];
+      const float* rsv = (const float*)(cur + S::RS);
+      const float* thv = (const float*)(cur + S::TH);
+      const float* dpv = (const float*)(cur + S::DOT);
+      const float dc = wave_sum(lane < wph ? dpv[lane] : 0.f);
       float rk[E], ps[E], sh[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int k = lane * E + e;
-        float v = 0.f;
-        for (int i = 0; i < NW; ++i) v += rp[i * Q + k];
-        rk[e] = v;
+        rk[e] = rsv[k];
         ps[e] = tsv[k];
-        sh[e] = ths[k];
+        float t = 0.f;
+#pragma unroll
+        for (int nt = 0; nt < nT; ++nt) t += thv[nt * Q + k];
+        sh[e] = t;
       }
       // suffix sums of T^h (over i >= k) and exclusive prefix sums of T^S
       // (over j < k): inside the lane, then across lanes
@@ -483,17 +488,9 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
         dD_part[((int64_t)b * nc + c) * H + h] = sd;
       }
     }
-    __syncthreads();
   }
 }
 
-// ---------------------------------------------------------------------------
-// chunk_bwd_wsum: the group's summed, masked interaction matrix
-//     Wsum[i][j] = sum_h M_h[i, j] dt_h,j (dy_h,i . x_h,j),   i >= j
-// one workgroup per (batch, chunk, group), float32 accumulators over the
-// group's heads, written once as bfloat16 triangle tiles.  It does not depend
-// on the state size, so the dB/dC kernel's column tiles share it.
-// ---------------------------------------------------------------------------
 // Issues the direct-to-LDS loads of one head's dY and x rows of the chunk
 // ([Q][64] each, t64 chunk order; rows past the sequence end repeat its last
 // row and must be masked by the consumer) and its cs and dt rows.
@@ -518,12 +515,27 @@ __device__ __forceinline__ void issue_rows_loads(uint32_t buf, const bf16* __res
 }
 
 template <int Q>
+struct WsLds {
+  static constexpr int BUF = 2 * Q * 128 + 2 * Q * 4;  // dY, x rows; cs, dt
+  static constexpr int RP = 2 * BUF;                    // rectangle-sum parts, 2 x [NW][Q]
+  static constexpr int BYTES = RP + 2 * BwdCfg<Q>::NW * Q * 4;
+  static_assert(2 * Q * 128 <= 2 * BUF, "setup slices of C and B fit in the head buffers");
+};
+
+// Per head also the rectangle sums of the log-decay gradient,
+//     R_k = sum_{i >= k > j} T_ij,   T_ij = (M o CB)_ij dt_j (dy_i . x_j),
+// from the same W tiles: the wave owns whole row strips, so it forms the
+// prefix sums of T along each of its rows (DPP scans inside a tile, a carry
+// across the strip) and adds, for every column k, the prefixes of its rows
+// i >= k; the per-wave column parts are summed after the head.
+template <int Q>
 __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
-    const bf16* __restrict__ x, const bf16* __restrict__ dy, const float* __restrict__ dA_cs,
-    const float* __restrict__ dt_T, bf16* __restrict__ wsum, int L, int H, int G, int nc) {
+    const bf16* __restrict__ x, const bf16* __restrict__ dy, const bf16* __restrict__ Bm,
+    const bf16* __restrict__ Cm, const float* __restrict__ dA_cs, const float* __restrict__ dt_T,
+    bf16* __restrict__ wsum, float* __restrict__ rsum, int L, int H, int G, int nc, int N) {
   using K = BwdCfg<Q>;
-  constexpr int P = 64, QT = K::QT, SLOTS = K::SLOTS;
-  constexpr int BUF = 2 * Q * 128 + 2 * Q * 4;  // dY, x rows; cs, dt
+  using S = WsLds<Q>;
+  constexpr int P = 64, QT = K::QT, NW = K::NW, NT = K::NT, SLOTS = K::SLOTS;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   int bid = blockIdx.x;
@@ -537,12 +549,56 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
   const int64_t tok0 = (int64_t)c * Q;
   const int64_t valid = (int64_t)L - tok0;
   const uint32_t base = lds_addr(smem);
+  float* rp = (float*)(smem + S::RP);
+
+  // ---- C B^T of the group on this wave's triangle tiles (float32)
+  f32x4 cb[SLOTS];
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) cb[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    const int L16 = lane & 15, grp = lane >> 4;
+    bf16* Cs = (bf16*)smem;
+    bf16* Bs = Cs + Q * 64;
+    const int64_t row0 = ((int64_t)b * L + tok0) * G + g;
+    for (int ns = 0; ns < N / 64; ++ns) {
+      __syncthreads();
+      load_rows64<Q, NT>(Cs, Cm + row0 * N + ns * 64, (int64_t)G * N, valid);
+      load_rows64<Q, NT>(Bs, Bm + row0 * N + ns * 64, (int64_t)G * N, valid);
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < SLOTS; ++k) {
+        const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 a = *(const bf16x8*)(Cs + t64(ti * 16 + L16, 32 * kk + 8 * grp));
+          const bf16x8 bb = *(const bf16x8*)(Bs + t64(tj * 16 + L16, 32 * kk + 8 * grp));
+          cb[k] = mfma16x16x32(a, bb, cb[k]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    for (int i = threadIdx.x; i < 2 * NW * Q; i += NT) rp[i] = 0.f;
+    __syncthreads();  // slices consumed before the head buffers take their space
+  }
 
   auto issue = [&](int h, int slot) {
     const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;
     const int64_t cb0 = (((int64_t)b * H + h) * nc + c) * Q;
-    issue_rows_loads<Q>(base + slot * BUF, dy + xrow0, x + xrow0, (int64_t)H * P, valid,
+    issue_rows_loads<Q>(base + slot * S::BUF, dy + xrow0, x + xrow0, (int64_t)H * P, valid,
                         dA_cs + cb0, dt_T + cb0);
+  };
+  // R of head h from the parts in rp[buf], which are zeroed for reuse
+  auto finish_rect = [&](int h, int buf) {
+    float* part = rp + buf * NW * Q;
+    float* out = rsum + (((int64_t)b * H + h) * nc + c) * Q;
+    for (int k = threadIdx.x; k < Q; k += NT) {
+      float v = 0.f;
+      for (int i = 0; i < NW; ++i) {
+        v += part[i * Q + k];
+        part[i * Q + k] = 0.f;
+      }
+      out[k] = v;
+    }
   };
 
   f32x4 ws[SLOTS];
@@ -553,16 +609,25 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
   for (int hh = 0; hh < HG; ++hh) {
     __builtin_amdgcn_s_waitcnt(0);  // this head's rows landed
     __syncthreads();                // ... for every wave; the other buffer is free
+    // (before the next head's loads are issued: anything the compiler waits
+    // for here would otherwise wait for them too)
+    if (hh > 0) finish_rect(g * HG + hh - 1, (hh - 1) & 1);
     if (hh + 1 < HG) issue(g * HG + hh + 1, (hh + 1) & 1);
-    const unsigned char* cur = smem + (hh & 1) * BUF;
+    const unsigned char* cur = smem + (hh & 1) * S::BUF;
     const bf16* Ys = (const bf16*)cur;
     const bf16* Xs = (const bf16*)(cur + Q * 128);
     const float* css = (const float*)(cur + 2 * Q * 128);
     const float* dts = css + Q;
+    float* part = rp + (hh & 1) * NW * Q + w * Q;
     const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
+    float carry[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < SLOTS; ++k) {
       const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
+      if (k == w + 1) {  // second row strip
+#pragma unroll
+        for (int r = 0; r < 4; ++r) carry[r] = 0.f;
+      }
       f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -572,16 +637,28 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
       }
       const int j = tj * 16 + L16;
       const float csj = css[j], dtj = dts[j];
+      float col = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = ti * 16 + 4 * grp + r;
-        const float e = fast_exp2(fminf(css[i] - csj, 0.f)) * dtj;
         // rows past the sequence end hold a repeated row: masked here
-        ws[k][r] += (i >= j && i < valid ? e : 0.f) * a4[r];
+        const float e = (i >= j && i < valid) ? fast_exp2(fminf(css[i] - csj, 0.f)) * dtj : 0.f;
+        const float wm = e * a4[r];
+        ws[k][r] += wm;
+        const float t = (i > j) ? cb[k][r] * wm : 0.f;
+        const float inc = row_scan16(t);
+        const float pm = carry[r] + row_prev(inc);  // sum_{j' < j} T[i][j'] along the row
+        carry[r] += __shfl(inc, 15, 16);
+        if (j <= i) col += pm;
       }
+      col += __shfl_xor(col, 16, 64);
+      col += __shfl_xor(col, 32, 64);
+      if (grp == 0) part[j] += col;
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  __syncthreads();
+  finish_rect(g * HG + HG - 1, (HG - 1) & 1);
 
   const int L16 = lane & 15, grp = lane >> 4;
   bf16* out = wsum + (((int64_t)b * nc + c) * G + g) * (int64_t)(K::NTILE * 256);
@@ -596,15 +673,15 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
 // ---------------------------------------------------------------------------
 // chunk_bwd_dbdc
 // ---------------------------------------------------------------------------
-// Q/16 waves: wave w owns output row tile w of dB and dC (row tile t has t+1
-// causal tiles for dC and Q/16-t for dB: Q/16+1 per tile, so every wave has
-// the same work).  Per head the wave's own rows of dY and x go straight to
-// registers in MFMA operand order, and the shared h and g column tiles, cs
-// and dt arrive by direct-to-LDS loads into a double buffer: the next head's
-// bytes are in flight while this head computes.
+// Q/32 waves: wave w owns output row tiles w and Q/16-1-w of dB and dC (row
+// tile t has t+1 causal tiles for dC and Q/16-t for dB: Q/16+1 per pair, so
+// every wave has the same work).  Per head the wave's own rows of dY and x go
+// straight to registers in MFMA operand order, loaded one head ahead, and the
+// shared h and g column tiles, cs and dt arrive by direct-to-LDS loads into a
+// double buffer: the next head's bytes are in flight while this head computes.
 template <int Q>
 struct BcCfg {
-  static constexpr int QT = Q / 16, NW = QT, NT = 64 * NW;
+  static constexpr int QT = Q / 16, NW = Q / 32, NT = 64 * NW;
 };
 
 template <int Q>
@@ -664,11 +741,9 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
 
   const int lane = lane_id();
   const int w = wave_id();
-  const int L16 = lane & 15, grp = lane >> 4;
   const int64_t tok0 = (int64_t)c * Q;
   const int64_t valid = (int64_t)L - tok0;
-  const int R = w;  // output row tile
-  const int row = R * 16 + L16;  // this lane's operand row
+  const int R[2] = {w, QT - 1 - w};  // output row tiles
 
   bf16* Bs = (bf16*)(smem + S::BS);
   bf16* Cs = (bf16*)(smem + S::CS);
@@ -679,16 +754,21 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
   };
   auto cs_of = [&](int h) { return (((int64_t)b * H + h) * nc + c) * (int64_t)Q; };
   // this lane's dY and x operand pieces of head h (zero past the sequence end)
-  auto load_rows = [&](int h, bf16x8 (&ay)[2], bf16x8 (&ax)[2]) {
-    const int rw = opaque(row);
-    const int64_t off = (((int64_t)b * L + tok0 + rw) * H + h) * P + 8 * opaque(grp);
+  bf16x8 nY[2][2], nX[2][2];
+  auto load_rows = [&](int h) {
+    const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      ay[kk] = zero8();
-      ax[kk] = zero8();
-      if (row < valid) {
-        ay[kk] = *(const bf16x8*)(dy + off + 32 * kk);
-        ax[kk] = *(const bf16x8*)(x + off + 32 * kk);
+    for (int s = 0; s < 2; ++s) {
+      const int row = R[s] * 16 + L16;
+      const int64_t off = (((int64_t)b * L + tok0 + row) * H + h) * P + 8 * grp;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        nY[s][kk] = zero8();
+        nX[s][kk] = zero8();
+        if (row < valid) {
+          nY[s][kk] = *(const bf16x8*)(dy + off + 32 * kk);
+          nX[s][kk] = *(const bf16x8*)(x + off + 32 * kk);
+        }
       }
     }
   };
@@ -696,84 +776,98 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
   const int h0 = g * HG;
   issue_head_loads<Q>(head_lds, hst + st_of(h0), gst + st_of(h0), N, dA_cs + cs_of(h0),
                       dt_T + cs_of(h0));
-  bf16x8 nY[2], nX[2];
-  load_rows(h0, nY, nX);
+  load_rows(h0);
   {
     const int64_t row0 = ((int64_t)b * L + tok0) * G + g;
     load_rows64<Q, NT>(Bs, Bm + row0 * N + nt * 64, (int64_t)G * N, valid);
     load_rows64<Q, NT>(Cs, Cm + row0 * N + nt * 64, (int64_t)G * N, valid);
   }
 
-  f32x4 accC[4], accB[4];
+  f32x4 accC[2][4], accB[2][4];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    accC[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accB[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      accC[s][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accB[s][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
   for (int hh = 0; hh < HG; ++hh) {
     const int h = h0 + hh;
-    // this head's buffer has landed (and every wave is done with the other one)
-    __builtin_amdgcn_s_waitcnt(0);  // every load of this wave, direct-to-LDS ones included
+    // this head's buffer and rows have landed (and every wave is done with
+    // the other buffer)
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const unsigned char* cur = smem + S::HEAD + (hh & 1) * S::BUF;
     const bf16* Hs = (const bf16*)cur;
     const bf16* Gs = (const bf16*)(cur + 8192);
     const float* css = (const float*)(cur + 16384);
     const float* dts = css + Q;
-    const bf16x8 aY[2] = {nY[0], nY[1]}, aX[2] = {nX[0], nX[1]};
+    bf16x8 aY[2][2], aX[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        aY[s][kk] = nY[s][kk];
+        aX[s][kk] = nX[s][kk];
+      }
     if (hh + 1 < HG) {
       issue_head_loads<Q>(head_lds + ((hh + 1) & 1) * S::BUF, hst + st_of(h + 1),
                           gst + st_of(h + 1), N, dA_cs + cs_of(h + 1), dt_T + cs_of(h + 1));
-      load_rows(h + 1, nY, nX);
+      load_rows(h + 1);
     }
 
     // state terms of this wave's rows: 2^cs_i (dY h)[i, n] into dC and
     // 2^(cs_last - cs_j) dt_j (X g)[j, n] into dB; T^h_i parts
     const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
     const float csL = css[Q - 1];
-    float eC[4], eB[4], thr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = R * 16 + 4 * grp + r;
-      eC[r] = fast_exp2(css[i]);
-      eB[r] = fast_exp2(csL - css[i]) * dts[i];
-      thr[r] = 0.f;
-    }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      f32x4 tc = f32x4{0.f, 0.f, 0.f, 0.f}, tb = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int r0 = 32 * kk + 8 * grp + (L16 >> 2), c0 = ct * 16 + 4 * (L16 & 3);
-        const int oa = t64(r0, c0), ob = t64(r0 + 4, c0);
-        const bf16x8 hb = cat(lds_read_tr(Hs + oa), lds_read_tr(Hs + ob));
-        const bf16x8 gb = cat(lds_read_tr(Gs + oa), lds_read_tr(Gs + ob));
-        tc = mfma16x16x32(aY[kk], hb, tc);
-        tb = mfma16x16x32(aX[kk], gb, tb);
-      }
+    for (int s = 0; s < 2; ++s) {
+      float eC[4], eB[4], thr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float vc = eC[r] * tc[r];
-        accC[ct][r] += vc;
-        accB[ct][r] += eB[r] * tb[r];
-        thr[r] += vc * bf2f(Cs[t64(R * 16 + 4 * grp + r, ct * 16 + L16)]);
+        const int i = R[s] * 16 + 4 * grp + r;
+        eC[r] = fast_exp2(css[i]);
+        eB[r] = fast_exp2(csL - css[i]) * dts[i];
+        thr[r] = 0.f;
       }
-    }
-    // T^h parts of this column tile: 2^cs_i dy_i . (h C_i) over its 64 columns
-    float* tho = th + ((((int64_t)b * nc + c) * H + h) * nT + nt) * Q + R * 16 + 4 * grp;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v = thr[r];
+      for (int ct = 0; ct < 4; ++ct) {
+        f32x4 tc = f32x4{0.f, 0.f, 0.f, 0.f}, tb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int mm = 1; mm < 16; mm <<= 1) v += __shfl_xor(v, mm, 64);
-      if (L16 == 0) tho[r] = v;
+        for (int kk = 0; kk < 2; ++kk) {
+          const int r0 = 32 * kk + 8 * grp + (L16 >> 2), c0 = ct * 16 + 4 * (L16 & 3);
+          const int oa = t64(r0, c0), ob = t64(r0 + 4, c0);
+          const bf16x8 hb = cat(lds_read_tr(Hs + oa), lds_read_tr(Hs + ob));
+          const bf16x8 gb = cat(lds_read_tr(Gs + oa), lds_read_tr(Gs + ob));
+          tc = mfma16x16x32(aY[s][kk], hb, tc);
+          tb = mfma16x16x32(aX[s][kk], gb, tb);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float vc = eC[r] * tc[r];
+          accC[s][ct][r] += vc;
+          accB[s][ct][r] += eB[r] * tb[r];
+          thr[r] += vc * bf2f(Cs[t64(R[s] * 16 + 4 * grp + r, ct * 16 + L16)]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // T^h parts of this column tile: 2^cs_i dy_i . (h C_i) over its 64 columns
+      float* tho = th + ((((int64_t)b * nc + c) * H + h) * nT + nt) * Q + R[s] * 16 + 4 * grp;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = thr[r];
+#pragma unroll
+        for (int mm = 1; mm < 16; mm <<= 1) v += __shfl_xor(v, mm, 64);
+        if (L16 == 0) tho[r] = v;
+      }
     }
   }
 
   // the group's summed W (bfloat16 triangle tiles) into LDS, then the
   // products with B and C
   __syncthreads();
+  const int L16 = lane & 15, grp = lane >> 4;
   bf16* Wt = (bf16*)(smem + S::HEAD);
   {
     const bf16* src = wsum + m * (int64_t)(BwdCfg<Q>::NTILE * 256);
@@ -782,8 +876,9 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
   }
   __syncthreads();
 
-  {
-    const int ti = R;  // dC rows: sum over j <= i
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int ti = R[s];  // dC rows: sum over j <= i
     for (int kp = 0; kp <= (ti >> 1); ++kp) {
       const int tj = 2 * kp + (grp >> 1);
       const bool live = tj <= ti;
@@ -794,10 +889,10 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
       for (int ct = 0; ct < 4; ++ct) {
         const int br = 32 * kp + 8 * grp + (L16 >> 2), bcol = ct * 16 + 4 * (L16 & 3);
         const bf16x8 bb = cat(lds_read_tr(Bs + t64(br, bcol)), lds_read_tr(Bs + t64(br + 4, bcol)));
-        accC[ct] = mfma16x16x32(a, bb, accC[ct]);
+        accC[s][ct] = mfma16x16x32(a, bb, accC[s][ct]);
       }
     }
-    const int tj = R;  // dB rows: sum over i >= j
+    const int tj = R[s];  // dB rows: sum over i >= j
     for (int kp = tj >> 1; kp < QT / 2; ++kp) {
       const int tii = 2 * kp + (grp >> 1);
       const bool live = tii >= tj;
@@ -809,23 +904,25 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
       for (int ct = 0; ct < 4; ++ct) {
         const int cr = 32 * kp + 8 * grp + (L16 >> 2), ccol = ct * 16 + 4 * (L16 & 3);
         const bf16x8 cc = cat(lds_read_tr(Cs + t64(cr, ccol)), lds_read_tr(Cs + t64(cr + 4, ccol)));
-        accB[ct] = mfma16x16x32(a, cc, accB[ct]);
+        accB[s][ct] = mfma16x16x32(a, cc, accB[s][ct]);
       }
     }
   }
 
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = R * 16 + 4 * grp + r;
-    if (i < valid) {
-      const int64_t o = (((int64_t)b * L + tok0 + i) * G + g) * N + nt * 64 + L16;
+  for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        dC[o + ct * 16] = f2bf(accC[ct][r]);
-        dB[o + ct * 16] = f2bf(accB[ct][r]);
+    for (int r = 0; r < 4; ++r) {
+      const int i = R[s] * 16 + 4 * grp + r;
+      if (i < valid) {
+        const int64_t o = (((int64_t)b * L + tok0 + i) * G + g) * N + nt * 64 + L16;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          dC[o + ct * 16] = f2bf(accC[s][ct][r]);
+          dB[o + ct * 16] = f2bf(accB[s][ct][r]);
+        }
       }
     }
-  }
 }
 
 // dA[h] and dD[h]: sums of the per-(batch, chunk) parts, one wave per head,
@@ -863,8 +960,8 @@ int cu_count_bwd() {
 template <int Q, int N>
 hipError_t launch_dx(const Dims& d, const void* x, const void* dy, const void* B, const void* C,
                      const float* dA_cs, const float* dt_T, const void* gst, const float* dots,
-                     int wph, const float* th, const float* A, const float* D, void* dx,
-                     void* ddt, float* dA_part, float* dD_part, hipStream_t s) {
+                     int wph, const float* th, const float* rsum, const float* A, const float* D,
+                     void* dx, void* ddt, float* dA_part, float* dD_part, hipStream_t s) {
   auto kern = chunk_bwd_dx_kernel<Q, N>;
   constexpr int lds = DxLds<Q, N>::BYTES;
   static const hipError_t attr =
@@ -879,7 +976,7 @@ hipError_t launch_dx(const Dims& d, const void* x, const void* dy, const void* B
   const int64_t grid = d.B * d.nc * d.G * slices;
   kern<<<(unsigned)grid, BwdCfg<Q>::NT, lds, s>>>(
       (const bf16*)x, (const bf16*)dy, (const bf16*)B, (const bf16*)C, dA_cs, dt_T,
-      (const bf16*)gst, dots, th, A, D, (bf16*)dx, (bf16*)ddt, dA_part, dD_part, (int)d.L,
+      (const bf16*)gst, dots, th, rsum, A, D, (bf16*)dx, (bf16*)ddt, dA_part, dD_part, (int)d.L,
       (int)d.H, (int)d.G, (int)d.nc, (int)hpw, (int)slices, wph);
   return hipGetLastError();
 }
@@ -887,15 +984,15 @@ hipError_t launch_dx(const Dims& d, const void* x, const void* dy, const void* B
 template <int Q>
 hipError_t launch_dbdc(const Dims& d, const void* x, const void* dy, const void* B, const void* C,
                        const float* dA_cs, const float* dt_T, const void* hst, const void* gst,
-                       void* wsum, void* dB, void* dC, float* th, hipStream_t s) {
+                       void* wsum, float* rsum, void* dB, void* dC, float* th, hipStream_t s) {
   auto wk = chunk_bwd_wsum_kernel<Q>;
-  constexpr int wlds = 2 * (2 * Q * 128 + 2 * Q * 4);
+  constexpr int wlds = WsLds<Q>::BYTES;
   static const hipError_t wattr =
       hipFuncSetAttribute((const void*)wk, hipFuncAttributeMaxDynamicSharedMemorySize, wlds);
   if (wattr != hipSuccess) return wattr;
   wk<<<(unsigned)(d.B * d.nc * d.G), BwdCfg<Q>::NT, wlds, s>>>(
-      (const bf16*)x, (const bf16*)dy, dA_cs, dt_T, (bf16*)wsum, (int)d.L, (int)d.H, (int)d.G,
-      (int)d.nc);
+      (const bf16*)x, (const bf16*)dy, (const bf16*)B, (const bf16*)C, dA_cs, dt_T, (bf16*)wsum,
+      rsum, (int)d.L, (int)d.H, (int)d.G, (int)d.nc, (int)d.N);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   auto kern = chunk_bwd_dbdc_kernel<Q>;
@@ -923,12 +1020,12 @@ bool backward_supported(const Dims& d) {
 hipError_t launch_chunk_bwd_dx(const Dims& d, const void* x, const void* dy, const void* B,
                                const void* C, const float* dA_cs, const float* dt_T,
                                const void* gst, const float* dots, int wph, const float* th,
-                               const float* A, const float* D, void* dx, void* ddt,
-                               float* dA_part, float* dD_part, hipStream_t s) {
-#define M2_DX(QQ, NN)                                                                       \
-  if (d.Q == QQ && d.N == NN)                                                               \
-    return launch_dx<QQ, NN>(d, x, dy, B, C, dA_cs, dt_T, gst, dots, wph, th, A, D, dx, ddt, \
-                             dA_part, dD_part, s);
+                               const float* rsum, const float* A, const float* D, void* dx,
+                               void* ddt, float* dA_part, float* dD_part, hipStream_t s) {
+#define M2_DX(QQ, NN)                                                                         \
+  if (d.Q == QQ && d.N == NN)                                                                 \
+    return launch_dx<QQ, NN>(d, x, dy, B, C, dA_cs, dt_T, gst, dots, wph, th, rsum, A, D, dx, \
+                             ddt, dA_part, dD_part, s);
   M2_DX(64, 64) M2_DX(64, 128) M2_DX(64, 256)
   M2_DX(128, 64) M2_DX(128, 128) M2_DX(128, 256)
   M2_DX(256, 64) M2_DX(256, 128) M2_DX(256, 256)
@@ -938,12 +1035,15 @@ hipError_t launch_chunk_bwd_dx(const Dims& d, const void* x, const void* dy, con
 
 hipError_t launch_chunk_bwd_dbdc(const Dims& d, const void* x, const void* dy, const void* B,
                                  const void* C, const float* dA_cs, const float* dt_T,
-                                 const void* hst, const void* gst, void* wsum, void* dB,
-                                 void* dC, float* th, hipStream_t s) {
+                                 const void* hst, const void* gst, void* wsum, float* rsum,
+                                 void* dB, void* dC, float* th, hipStream_t s) {
   switch (d.Q) {
-    case 64: return launch_dbdc<64>(d, x, dy, B, C, dA_cs, dt_T, hst, gst, wsum, dB, dC, th, s);
-    case 128: return launch_dbdc<128>(d, x, dy, B, C, dA_cs, dt_T, hst, gst, wsum, dB, dC, th, s);
-    case 256: return launch_dbdc<256>(d, x, dy, B, C, dA_cs, dt_T, hst, gst, wsum, dB, dC, th, s);
+    case 64:
+      return launch_dbdc<64>(d, x, dy, B, C, dA_cs, dt_T, hst, gst, wsum, rsum, dB, dC, th, s);
+    case 128:
+      return launch_dbdc<128>(d, x, dy, B, C, dA_cs, dt_T, hst, gst, wsum, rsum, dB, dC, th, s);
+    case 256:
+      return launch_dbdc<256>(d, x, dy, B, C, dA_cs, dt_T, hst, gst, wsum, rsum, dB, dC, th, s);
     default: return hipErrorInvalidValue;
   }
 }

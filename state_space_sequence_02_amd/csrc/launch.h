@@ -51,16 +51,17 @@ hipError_t launch_state_passing_reverse(const Dims& d, const float* E, const flo
                                         float* dh0, float* dots, hipStream_t s);
 // dB, dC, and th[B,nc,H,N/64,Q]: per state-column tile parts of
 // 2^cs_i dy_i . (h_c C_i), the carried-state term of y_i weighted by dy_i.
-// wsum: [B,nc,G] blocks of Q(Q+16)/2 bf16 (the group's summed W triangle).
+// wsum: [B,nc,G] blocks of Q(Q+16)/2 bf16 (the group's summed W triangle);
+// rsum [B,H,nc,Q] f32: the rectangle sums of the log-decay gradient.
 hipError_t launch_chunk_bwd_dbdc(const Dims& d, const void* x, const void* dy, const void* B,
                                  const void* C, const float* dA_cs, const float* dt_T,
-                                 const void* hst, const void* gst, void* wsum, void* dB,
-                                 void* dC, float* th, hipStream_t s);
+                                 const void* hst, const void* gst, void* wsum, float* rsum,
+                                 void* dB, void* dC, float* th, hipStream_t s);
 hipError_t launch_chunk_bwd_dx(const Dims& d, const void* x, const void* dy, const void* B,
                                const void* C, const float* dA_cs, const float* dt_T,
                                const void* gst, const float* dots, int wph, const float* th,
-                               const float* A, const float* D, void* dx, void* ddt,
-                               float* dA_part, float* dD_part, hipStream_t s);
+                               const float* rsum, const float* A, const float* D, void* dx,
+                               void* ddt, float* dA_part, float* dD_part, hipStream_t s);
 hipError_t launch_bwd_param_sums(const Dims& d, const float* dA_part, const float* dD_part,
                                  float* dA, float* dD, hipStream_t s);
 
