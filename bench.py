@@ -289,7 +289,28 @@ def decode_bench(args):
         "data": "synthetic", "config": {"workload": w.name, "batch": w.batch},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "cpu_baseline": None if args.no_cpu_baseline else decode_cpu_baseline(inp, w),
     }), flush=True)
+
+
+def decode_cpu_baseline(inp, w):
+    """The CPU oracle advancing the same batch by one token (its recurrence
+    over a one-token sequence from the given state), repeated for at least a
+    second; tokens/s over the batch."""
+    import oracle
+    o = {k: (None if v is None else v.float().numpy()) for k, v in inp.items()}
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ssd_recurrence(o["x"], o["dt"], o["A"], o["B"], o["C"], o["D"], o["init_state"],
+                              chunk_size=64, want_final=True)
+        reps += 1
+        sec = time.perf_counter() - t0
+        if sec >= 1.0:
+            break
+    return {"value": w.batch * reps / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": sec,
+            "sample": f"{reps} one-token steps of the whole batch ({w.batch} sequences, "
+                      f"{w.nheads} heads)"}
 
 
 BWD_STAGES = ("chunk_cumsum", "chunk_state", "state_passing", "adjoint_state", "reverse_pass",
