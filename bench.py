@@ -335,10 +335,14 @@ def backward_model(w):
     m["adjoint_state"] = dict(flops=2 * N * P * tok * H, bytes=x + bc + 2 * csb + st)
     m["reverse_pass"] = dict(flops=2 * st // 4 + 2 * st // 4,
                              bytes=st + hs + B * H * nc * 4 + 2 * fin + hs)
-    m["dB_dC"] = dict(flops=tok * H * ((Q + 1) * P + 4 * P * N) + tok * G * 2 * (Q + 1) * N,
-                      bytes=2 * x + 2 * bc + 2 * hs + 2 * csb + 2 * bc + th)
-    m["dx"] = dict(flops=tok * G * (Q + 1) * N + tok * H * (2 * P * N + 2 * (Q + 1) * P),
-                   bytes=2 * x + 2 * bc + hs + 2 * csb + th + x + tok * H * 2)
+    rs = B * H * nc * Q * 4                           # rectangle sums of the decay gradient
+    # dB_dC: the summed-W kernel (W, its rectangle sums, C B^T once per
+    # (chunk, group)) and the dB/dC kernel (state terms, summed W times B, C)
+    m["dB_dC"] = dict(
+        flops=tok * H * ((Q + 1) * P + 4 * P * N) + tok * G * 3 * (Q + 1) * N,
+        bytes=2 * x + 2 * bc + 2 * hs + 2 * csb + 2 * bc + th + rs)
+    m["dx"] = dict(flops=tok * G * (Q + 1) * N + tok * H * (2 * P * N + (Q + 1) * P),
+                   bytes=2 * x + 2 * bc + hs + 2 * csb + th + rs + x + tok * H * 2)
     m["param_sums"] = dict(flops=4 * B * nc * H, bytes=2 * B * nc * H * 4 + 2 * H * 4)
     return m
 

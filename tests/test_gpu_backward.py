@@ -42,6 +42,8 @@ SHAPES = [
     _w("bwd_Q256_N64_H8_G1", 512, 8, 64, 1, 256, init=False, seed=66),
     _w("bwd_Q256_N128_H6_G3", 700, 6, 128, 3, 256, seed=67),
     _w("bwd_Q64_N128_G1_H8", 333, 8, 128, 1, 64, seed=68),
+    _w("bwd_one_token", 1, 4, 128, 2, 128, Bn=2, seed=72),
+    _w("bwd_Q128_N256_heads_eq_groups", 257, 3, 256, 3, 128, Bn=3, seed=73),
 ]
 
 NAMES = ("dx", "ddt", "dA", "dB", "dC", "dD", "dinit")
