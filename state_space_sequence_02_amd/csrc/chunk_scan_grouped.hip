@@ -134,13 +134,16 @@ __device__ __forceinline__ void weights4(bf16x8& gm, int half, const f32x4 gt, c
 // each pair's x operand and weight exponents a single time and applying them
 // to every i-tile at or below the pair.  G^T tile (jt, t0) sits in slot jt,
 // (jt, t1) in slot QT - jt.
+// L16 and grp (the lane's position in its 16-lane row and its row) come from
+// the caller, hidden from the optimiser per head: otherwise it hoists every
+// diagonal-tile comparison out of the head loop as a 64-bit lane mask, runs
+// out of scalar registers and reloads the masks from spill lanes at each use.
 template <int QT, int P>
 __device__ __forceinline__ void in_chunk(const f32x4 (&Gs)[QT + 1], f32x4 (&Y0)[P / 16],
                                          f32x4 (&Y1)[P / 16], int t0, int t1, const float* css,
-                                         const float* lws, const unsigned char* Xs, float Dh) {
+                                         const float* lws, const unsigned char* Xs, float Dh,
+                                         int L16, int grp) {
   constexpr int PT = P / 16;
-  const int lane = lane_id();
-  const int L16 = lane & 15, grp = lane >> 4;
   const int i0 = 16 * t0 + L16, i1 = 16 * t1 + L16;
   const float cs0 = css[i0], cs1 = css[i1];
   const float sc0 = fast_exp2(cs0), sc1 = fast_exp2(cs1);
@@ -343,7 +346,9 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
     }
     lds_barrier();  // weights visible; next head's loads stay in flight
     const float Dh = Dv ? Dv[h] : 0.f;
-    in_chunk<QT, P>(Gs, Y[0], Y[1], t0, t1, css, dts, Xs, Dh);
+    int l16 = L16, lgrp = grp;
+    asm volatile("" : "+v"(l16), "+v"(lgrp));
+    in_chunk<QT, P>(Gs, Y[0], Y[1], t0, t1, css, dts, Xs, Dh, l16, lgrp);
 
     __builtin_amdgcn_s_waitcnt(0);  // next head's bytes have landed (and older stores drained)
     const int64_t valid = L - tok0;
