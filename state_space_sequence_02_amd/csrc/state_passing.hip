@@ -73,6 +73,25 @@ __global__ void __launch_bounds__(kThreads) state_passing_kernel(
   if (final_state) ((V*)final_state)[bh * PNv + gid] = run;
 }
 
+// v + (v of the lane the DPP control selects), 0 where no lane is selected.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false);
+  return v + __builtin_bit_cast(float, s);
+}
+
+// Sum over the wavefront's 64 lanes, complete in lane 63: a scan inside each
+// 16-lane row (row_shr 1, 2, 4, 8), then the row totals carried upwards
+// (row_bcast 15, 31) - cross-lane VALU paths instead of LDS permutes.
+__device__ __forceinline__ float wave_total_in_lane63(float v) {
+  v = dpp_add<0x111, 0xf>(v);
+  v = dpp_add<0x112, 0xf>(v);
+  v = dpp_add<0x114, 0xf>(v);
+  v = dpp_add<0x118, 0xf>(v);
+  v = dpp_add<0x142, 0xa>(v);
+  return dpp_add<0x143, 0xc>(v);
+}
+
 // Backward pass: the same jump run in reverse chunk order on the adjoint.
 // With r_c the gradient of the loss with respect to the start state of
 // chunk c, r_nc = dfinal and r_c = 2^cs_last(c) r_{c+1} + E_c, where E_c is
@@ -135,9 +154,8 @@ __global__ void __launch_bounds__(kThreads) state_passing_reverse_kernel(
         }
         const float decay = exp2f(cs_last[(int64_t)c * Q]);
         float part = live ? run[0] * hc[0] + run[1] * hc[1] + run[2] * hc[2] + run[3] * hc[3] : 0.f;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-        if ((threadIdx.x & 63) == 0) dot_out[(int64_t)c * wph] = decay * part;
+        part = wave_total_in_lane63(part);
+        if ((threadIdx.x & 63) == 63) dot_out[(int64_t)c * wph] = decay * part;
         run = decay * run + cur;
       }
     }
