@@ -78,6 +78,8 @@ def main():
                          "(H=32, P=64, N=256, bf16)")
     ap.add_argument("--backward", action="store_true",
                     help="only measure the backward pass (mamba2_ssd_backward) on the workload")
+    ap.add_argument("--state-path", choices=("default", "fused"), default="default",
+                    help="fused: measure mamba2_ssd_forward_fused (one-kernel fwd_pass_state)")
     args = ap.parse_args()
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
@@ -96,6 +98,9 @@ def main():
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.state_path == "fused":
+        fused_state_bench(args)
+        return
 
     import torch
 
@@ -184,6 +189,103 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+def fused_state_model(w):
+    """Algorithmic flops and HBM bytes of one mamba2_fwd_pass_state call: the
+    weights kernel (reads the cumulative sums and dt, writes the weights) and
+    the one-kernel state pass (reads x, B, the sums and weights, writes the
+    bfloat16 chunk-start states and the float32 final state).  Every head of a
+    group reads the group's B rows, so B counts once per head."""
+    B, L, H, P, N, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk_size
+    tok, csb = B * L, B * H * w.nchunks * Q * 4
+    hs = B * w.nchunks * H * P * N * 2
+    fin = B * H * P * N * 4
+    init = fin if w.init_state else 0
+    return dict(flops=2 * N * P * tok * H,
+                bytes=3 * csb + tok * H * P * 2 + tok * H * N * 2 + 2 * csb + hs + fin + init)
+
+
+def fused_state_bench(args):
+    import torch
+
+    import ssd_inputs
+    import state_space_sequence_02_amd as m2
+
+    w = ssd_inputs.WORKLOADS[args.workload]
+    inp = ssd_inputs.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    dims = m2.dims_of(g["x"], g["B"], w.chunk_size)
+    y = torch.empty_like(g["x"])
+    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    need = m2.mamba2_ssd_workspace_bytes(dims)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        m2.mamba2_ssd_forward_fused(dims, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"],
+                                    g["init_state"], y, fin, ws, need, stream)
+
+    def timed(fn, n):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(n):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = timed(step, args.steps)
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # the state pass alone, on the same stream: weights kernel + one-kernel pass
+    cs, dtt, _ = m2.stage_buffers(dims, dev)
+    m2.mamba2_chunk_cumsum(dims, g["dt"], g["A"], cs, dtt, stream)
+    wT = torch.empty_like(cs)
+    hst = torch.empty((w.batch, w.nchunks, w.nheads, w.headdim, w.dstate), dtype=torch.bfloat16,
+                      device=dev)
+    fin2 = torch.empty_like(fin)
+
+    def state_pass():
+        m2.mamba2_fwd_pass_state(dims, g["x"], g["B"], cs, dtt, g["init_state"], wT, hst, fin2,
+                                 stream)
+
+    state_pass()
+    torch.cuda.synchronize()
+    sp_ms = timed(state_pass, args.steps)
+    dm = fused_state_model(w)
+    achieved = dm["bytes"] / (sp_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": w.tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "wall_ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk_size": w.chunk_size, "state_path": "one-kernel fwd_pass_state",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "fwd_pass_state (weights + state pass)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": dm["bytes"], "algorithmic_flops": dm["flops"],
+                     "ms": sp_ms, "TFLOP/s": dm["flops"] / (sp_ms * 1e-3) / 1e12},
+    }
     print(json.dumps(out), flush=True)
 
 

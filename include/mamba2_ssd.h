@@ -182,6 +182,39 @@ int mamba2_ssd_forward_profile(const mamba2_dims* dims, const void* x, const voi
                                float* stage_ms);
 
 /*
+ * fwd_pass_state as one kernel, the pages' own second kernel (devotd.net news
+ * item, section 2: the state at every chunk start and after the last chunk,
+ * chunk order kept while independent parts of the state run in parallel;
+ * disconfirmai.com, body: the jump formula with exponentially pre-scaled rows
+ * of X): per state tile, walks the chunks in order with the running state in
+ * float32 MFMA accumulators, so the per-chunk states never reach memory.
+ * Inputs: x, B, dA_cs, dt_T (from mamba2_chunk_cumsum), init_state (NULL =
+ * zeros).  Outputs: w_T [B,H,nc,Q] float32, the contraction weights
+ * 2^(cs[Q-1] - cs[j]) * dt_j (written first, then read by the kernel);
+ * chunk_start_states [B,nc,H,P,N] bfloat16 (round to nearest even);
+ * final_state [B,H,P,N] float32.  Supported: bfloat16 with headdim 64,
+ * dstate 64, 128 or 256 and chunk_size 64, 128 or 256 (UNSUPPORTED
+ * otherwise).  The default forward (chunk_state + state_passing) is faster on
+ * this chip; this path is the one-kernel form for callers that want it.
+ */
+int mamba2_fwd_pass_state(const mamba2_dims* dims, const void* x, const void* B,
+                          const float* dA_cs, const float* dt_T, const float* init_state,
+                          float* w_T, void* chunk_start_states, float* final_state,
+                          void* stream);
+
+/*
+ * The whole forward through the one-kernel fwd_pass_state: chunk_cumsum ->
+ * weights -> fwd_pass_state -> chunk_scan.  Same arguments, results (up to
+ * rounding order) and workspace as mamba2_ssd_forward (at least
+ * mamba2_ssd_workspace_bytes(dims)); final_state is required.  Sizes as for
+ * mamba2_fwd_pass_state.
+ */
+int mamba2_ssd_forward_fused(const mamba2_dims* dims, const void* x, const void* dt,
+                             const float* A, const void* B, const void* C, const float* D,
+                             const float* init_state, void* y, float* final_state,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Recurrent single-token step: the constant-memory inference mode of the same
  * recurrence (pages: devotd.net news item, section 1 - a fixed-size hidden
  * state updated as tokens are processed; disconfirmai.com, abstract - the

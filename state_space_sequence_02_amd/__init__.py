@@ -39,7 +39,8 @@ MAMBA2_DTYPE_BF16 = 1
 EXPORTS = (
     "mamba2_validate", "mamba2_chunk_cumsum", "mamba2_chunk_state", "mamba2_state_passing",
     "mamba2_chunk_scan", "mamba2_ssd_workspace_bytes", "mamba2_ssd_forward",
-    "mamba2_ssd_forward_profile", "mamba2_decode_step", "mamba2_ssd_backward_workspace_bytes",
+    "mamba2_ssd_forward_profile", "mamba2_fwd_pass_state", "mamba2_ssd_forward_fused",
+    "mamba2_decode_step", "mamba2_ssd_backward_workspace_bytes",
     "mamba2_ssd_backward", "mamba2_ssd_backward_profile", "mamba2_status_string",
     "mamba2_last_error",
 )
@@ -81,6 +82,9 @@ def _load():
         "mamba2_ssd_forward_profile": ([D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
                                         ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
         "mamba2_decode_step": ([D, P, P, P, P, P, P, P, P, P], ctypes.c_int),
+        "mamba2_fwd_pass_state": ([D, P, P, P, P, P, P, P, P, P], ctypes.c_int),
+        "mamba2_ssd_forward_fused": ([D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P],
+                                     ctypes.c_int),
         "mamba2_ssd_backward_workspace_bytes": ([D], ctypes.c_size_t),
         "mamba2_ssd_backward": ([D] + [P] * 17 + [ctypes.c_size_t, P], ctypes.c_int),
         "mamba2_ssd_backward_profile": ([D] + [P] * 17 + [ctypes.c_size_t, P, P], ctypes.c_int),
@@ -191,6 +195,24 @@ def mamba2_ssd_forward_profile(dims, x, dt, A, B, C, D, init_state, y, final_sta
                                            int(workspace_bytes), _stream(stream), ms),
            "mamba2_ssd_forward_profile")
     return [float(v) for v in ms]
+
+
+def mamba2_fwd_pass_state(dims, x, B, dA_cs, dt_T, init_state, w_T, chunk_start_states,
+                          final_state, stream=None):
+    _check(_lib.mamba2_fwd_pass_state(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(dA_cs),
+                                      _ptr(dt_T), _ptr(init_state), _ptr(w_T),
+                                      _ptr(chunk_start_states), _ptr(final_state),
+                                      _stream(stream)),
+           "mamba2_fwd_pass_state")
+
+
+def mamba2_ssd_forward_fused(dims, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                             workspace_bytes, stream=None):
+    _check(_lib.mamba2_ssd_forward_fused(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                         _ptr(C), _ptr(D), _ptr(init_state), _ptr(y),
+                                         _ptr(final_state), _ptr(workspace),
+                                         int(workspace_bytes), _stream(stream)),
+           "mamba2_ssd_forward_fused")
 
 
 def mamba2_decode_step(dims, x, dt, A, B, C, D, state, y, stream=None):

@@ -331,6 +331,61 @@ int check_backward_args(const mamba2_dims* dims, m2::Dims* d, const void* x, con
 
 extern "C" {
 
+int mamba2_fwd_pass_state(const mamba2_dims* dims, const void* x, const void* B,
+                          const float* dA_cs, const float* dt_T, const float* init_state,
+                          float* w_T, void* chunk_start_states, float* final_state,
+                          void* stream) {
+  m2::Dims d;
+  CHECK(validate(dims, &d));
+  if (!m2::fused_state_supported(d))
+    return fail(MAMBA2_ERR_UNSUPPORTED,
+                "fwd_pass_state needs bfloat16, headdim 64, dstate 64/128/256 and chunk_size "
+                "64/128/256");
+  CHECK(need(x, "x"));
+  CHECK(need(B, "B"));
+  CHECK(need(dA_cs, "dA_cs"));
+  CHECK(need(dt_T, "dt_T"));
+  CHECK(maybe(init_state, "init_state"));
+  CHECK(need(w_T, "w_T"));
+  CHECK(need(chunk_start_states, "chunk_start_states"));
+  CHECK(need(final_state, "final_state"));
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = m2::launch_chunk_weights(d, dA_cs, dt_T, w_T, s);
+  if (e == hipSuccess)
+    e = m2::launch_fwd_pass_state(d, x, B, dA_cs, w_T, init_state, chunk_start_states,
+                                  final_state, s);
+  return hip_status(e, "fwd_pass_state launch");
+}
+
+int mamba2_ssd_forward_fused(const mamba2_dims* dims, const void* x, const void* dt,
+                             const float* A, const void* B, const void* C, const float* D,
+                             const float* init_state, void* y, float* final_state,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  m2::Dims d;
+  CHECK(check_forward_args(dims, &d, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                           workspace_bytes));
+  if (!m2::fused_state_supported(d))
+    return fail(MAMBA2_ERR_UNSUPPORTED,
+                "the one-kernel fwd_pass_state needs bfloat16, headdim 64, dstate 64/128/256 "
+                "and chunk_size 64/128/256");
+  if (!final_state) return fail(MAMBA2_ERR_NULL, "final_state is NULL");
+  // workspace: dA_cs, dt_T, w_T [B,H,nc,Q] f32, then the bf16 chunk-start
+  // states (inside the default forward's workspace size)
+  const Workspace w = plan(d);
+  char* ws = (char*)workspace;
+  float* dA_cs = (float*)ws;
+  float* dt_T = (float*)(ws + w.cs_bytes);
+  float* w_T = (float*)(ws + 2 * w.cs_bytes);
+  void* hst = ws + 3 * w.cs_bytes;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = m2::launch_chunk_cumsum(d, dt, A, dA_cs, dt_T, s);
+  if (e == hipSuccess) e = m2::launch_chunk_weights(d, dA_cs, dt_T, w_T, s);
+  if (e == hipSuccess)
+    e = m2::launch_fwd_pass_state(d, x, B, dA_cs, w_T, init_state, hst, final_state, s);
+  if (e == hipSuccess) e = m2::launch_chunk_scan_grouped(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
+  return hip_status(e, "ssd_forward_fused launch");
+}
+
 size_t mamba2_ssd_backward_workspace_bytes(const mamba2_dims* dims) {
   m2::Dims d;
   if (validate(dims, &d) != MAMBA2_OK || !m2::backward_supported(d)) return 0;

@@ -65,6 +65,16 @@ hipError_t launch_chunk_bwd_dx(const Dims& d, const void* x, const void* dy, con
 hipError_t launch_bwd_param_sums(const Dims& d, const float* dA_part, const float* dD_part,
                                  float* dA, float* dD, hipStream_t s);
 
+// fwd_pass_state as one kernel (bfloat16, P = 64, N in {64, 128, 256},
+// Q in {64, 128, 256}): chunk-start states to hst (bf16 [B,nc,H,P,N]) and the
+// final state, from the weights w_T = 2^(cs_last - cs_j) dt_j [B,H,nc,Q].
+bool fused_state_supported(const Dims& d);
+hipError_t launch_chunk_weights(const Dims& d, const float* dA_cs, const float* dt_T, float* w_T,
+                                hipStream_t s);
+hipError_t launch_fwd_pass_state(const Dims& d, const void* x, const void* B, const float* dA_cs,
+                                 const float* w_T, const float* init, void* hst,
+                                 float* final_state, hipStream_t s);
+
 // One-token recurrent step, in place on the float32 state [B,H,P,N];
 // x, y [B,H,P], dt [B,H], B, C [B,G,N].
 hipError_t launch_decode_step(const Dims& d, const void* x, const void* dt, const float* A,

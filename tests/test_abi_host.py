@@ -160,3 +160,36 @@ def test_backward_checks_on_host():
     need = m2.mamba2_ssd_backward_workspace_bytes(d)
     assert call(d, wsb=need - 1) == m2.MAMBA2_ERR_WORKSPACE
     assert "needed" in m2.mamba2_last_error()
+
+
+def test_fused_state_checks_on_host():
+    lib = m2._lib
+    ok = 1 << 20
+    big = 1 << 40
+    d = _dims()
+
+    def fused(dims, **over):
+        args = dict(x=ok, dt=ok, A=ok, B=ok, C=ok, D=None, h0=None, y=ok, fin=ok, ws=ok,
+                    wsb=big)
+        args.update(over)
+        return lib.mamba2_ssd_forward_fused(ctypes.byref(dims), *args.values(), 0)
+
+    def fps(dims, **over):
+        args = dict(x=ok, B=ok, cs=ok, dtt=ok, h0=None, wT=ok, hst=ok, fin=ok)
+        args.update(over)
+        return lib.mamba2_fwd_pass_state(ctypes.byref(dims), *args.values(), 0)
+
+    # valid forward sizes the one-kernel state pass does not cover
+    for kw in (dict(dtype=m2.MAMBA2_DTYPE_F32, headdim=16, dstate=16, nheads=2, chunk_size=64),
+               dict(headdim=32), dict(dstate=512)):
+        dd = _dims(**kw)
+        assert m2.mamba2_validate(dd) == m2.MAMBA2_OK
+        assert fused(dd) == m2.MAMBA2_ERR_UNSUPPORTED
+        assert fps(dd) == m2.MAMBA2_ERR_UNSUPPORTED
+    assert fused(d, fin=None) == m2.MAMBA2_ERR_NULL and "final" in m2.mamba2_last_error()
+    assert fused(d, ws=None) == m2.MAMBA2_ERR_WORKSPACE
+    need = m2.mamba2_ssd_workspace_bytes(d)
+    assert fused(d, wsb=need - 1) == m2.MAMBA2_ERR_WORKSPACE
+    assert fps(d, wT=None) == m2.MAMBA2_ERR_NULL and "w_T" in m2.mamba2_last_error()
+    assert fps(d, hst=ok + 4) == m2.MAMBA2_ERR_ALIGN
+    assert fps(d, h0=ok + 8) == m2.MAMBA2_ERR_ALIGN and "init" in m2.mamba2_last_error()
