@@ -1,7 +1,8 @@
 """Benchmark of the chunked Mamba-2 SSD forward pass on one MI355X.
 
-One step = one mamba2_ssd_forward (chunk_cumsum -> chunk_state ->
-state_passing -> chunk_scan) over the whole workload, inputs resident in HBM.
+One step = one mamba2_ssd_forward (chunk_cumsum -> fwd_pass_state ->
+chunk_scan; at L = 64K fwd_pass_state runs over spans of chunks: span_end ->
+span_pass) over the whole workload, inputs resident in HBM.
 Prints one JSON line with tokens/s, the roofline position of the dominant
 kernel (per-kernel durations measured here with HIP events on the launch
 stream) and the CPU oracle's throughput on the host as a reported baseline.
@@ -36,12 +37,40 @@ def grouped_path(w):
             and w.chunk_size in (64, 128, 256))
 
 
-def stage_model(w):
+def span_plan(w, cus=256):
+    """(span length K, heads per workgroup R) of the forward's span path, or
+    None where the library runs chunk_state + state_passing (same rule as
+    the library's dispatch: spans of 8, else 4, chunks while the grid gives
+    every CU a workgroup; R = 4, 2 or 1 heads of a group likewise)."""
+    if not grouped_path(w):
+        return None
+    nc = w.nchunks
+    for K in (8, 4):
+        ng = -(-nc // K)
+        if nc >= K and w.batch * w.nheads * ng >= cus:
+            for R in (4, 2):
+                if (w.nheads // w.ngroups) % R == 0 and w.batch * ng * w.nheads // R >= cus:
+                    return K, R
+            return K, 1
+    return None
+
+
+def forward_stages(w, cus=256):
+    """Names of the four timed slots of mamba2_ssd_forward_profile."""
+    if span_plan(w, cus):
+        return ("chunk_cumsum", "span_end", "span_pass", "chunk_scan")
+    return STAGES
+
+
+def stage_model(w, cus=256):
     """Algorithmic flops and HBM bytes per launch of each stage of the fused
     forward: every input read once and every output written once, in the
     dtypes that stage consumes and produces; flops count the causal triangle
     (diagonal included) and nothing above it, and the C B^T products once per
-    (chunk, group), since every head of the group shares them."""
+    (chunk, group), since every head of the group shares them.  On the span
+    path, span_end is the span-end kernel and span_pass the jump across spans
+    plus the replay that writes the chunk-start states (x rows of every
+    chunk but each span's last, which needs no contraction)."""
     B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
     nc = w.nchunks
     e = 4 if w.dtype == "f32" else 2
@@ -59,6 +88,18 @@ def stage_model(w):
         # C B^T depends only on the (chunk, group): counted once per group
         flops=tok * H * (2 * N * P + (Q + 1) * P + 2 * P) + tok * G * (Q + 1) * N,
         bytes=x + 2 * bc + 2 * csb + hs + H * 4 + x)
+    plan = span_plan(w, cus)
+    if plan:
+        K = plan[0]
+        ng = -(-nc // K)
+        ss = B * ng * H * P * N * 4                  # span states, float32
+        dec = B * H * ng * 4
+        init = fin if w.init_state else 0
+        frac = (nc - ng) / nc                         # chunks the replay contracts
+        m["span_end"] = dict(flops=2 * N * P * tok * H, bytes=x + bc + 2 * csb + ss + dec)
+        m["span_pass"] = dict(
+            flops=2 * ss // 4 + 2 * N * P * tok * H * frac,
+            bytes=(ss + dec + init + ss + fin) + (x * frac + bc * frac + 2 * csb + ss + hs))
     return m
 
 
@@ -143,9 +184,11 @@ def main():
         ms4 = m2.mamba2_ssd_forward_profile(dims, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"],
                                             g["init_state"], y, fin, ws, need, stream)
         stage_sum = [a + b for a, b in zip(stage_sum, ms4)]
-    stage_ms = {s: stage_sum[i] / args.steps for i, s in enumerate(STAGES)}
-    model = stage_model(w)
-    dom = max(STAGES, key=lambda s: stage_ms[s])
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    names = forward_stages(w, cus)
+    stage_ms = {s: stage_sum[i] / args.steps for i, s in enumerate(names)}
+    model = stage_model(w, cus)
+    dom = max(names, key=lambda s: stage_ms[s])
     dm = model[dom]
     ai = dm["flops"] / dm["bytes"]
     bound = "hbm" if ai < RIDGE else "mfma"
@@ -156,7 +199,7 @@ def main():
         achieved = dm["flops"] / (stage_ms[dom] * 1e-3) / 1e12
         peak, unit = BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
     stages = {}
-    for s in STAGES:
+    for s in names:
         t = stage_ms[s] * 1e-3
         stages[s] = {"ms": round(stage_ms[s], 4),
                      "GB/s": round(model[s]["bytes"] / t / 1e9, 1),
@@ -295,6 +338,8 @@ KERNEL_SOURCES = {
     "chunk_cumsum": ("chunk_cumsum.hip", "common.h"),
     "chunk_state": ("chunk_state_grouped.hip", "common.h"),
     "state_passing": ("state_passing.hip", "common.h"),
+    "span_end": ("state_span.hip", "common.h"),
+    "span_pass": ("state_span.hip", "common.h"),
     "chunk_scan": ("chunk_scan_grouped.hip", "common.h"),
     "adjoint_state": ("chunk_state_grouped.hip", "common.h"),
     "reverse_pass": ("state_passing.hip", "common.h"),

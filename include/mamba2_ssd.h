@@ -156,12 +156,18 @@ int mamba2_chunk_scan(const mamba2_dims* dims, const void* x, const void* B,
 size_t mamba2_ssd_workspace_bytes(const mamba2_dims* dims);
 
 /*
- * The whole forward pass: chunk_cumsum -> chunk_state -> state_passing ->
- * chunk_scan on `stream`, intermediates in the caller's workspace (at least
+ * The whole forward pass: chunk_cumsum -> fwd_pass_state -> chunk_scan on
+ * `stream`, intermediates in the caller's workspace (at least
  * mamba2_ssd_workspace_bytes(dims) bytes, 256-byte aligned; contents on
  * return are unspecified).  init_state and D may be NULL; final_state may
  * be NULL (not written).  Outputs y [B,L,H,P] (dtype of dims) and
- * final_state [B,H,P,N] float32.
+ * final_state [B,H,P,N] float32.  fwd_pass_state runs as chunk_state ->
+ * state_passing, or, for bfloat16 with headdim 64, dstate 64/128/256 and
+ * enough (batch, head, span) work to fill the device, over spans of 8 (or
+ * 4) chunks (devotd.net news item, section 2: the same jump across chunks,
+ * taken span by span): the state after each span from a zero start, the
+ * jump across spans, then each span replayed from its start state to give
+ * the chunk-start states.  Both give the same result up to rounding order.
  */
 int mamba2_ssd_forward(const mamba2_dims* dims, const void* x, const void* dt,
                        const float* A, const void* B, const void* C, const float* D,
@@ -171,8 +177,10 @@ int mamba2_ssd_forward(const mamba2_dims* dims, const void* x, const void* dt,
 /*
  * Same as mamba2_ssd_forward, then waits for the work to finish and writes
  * the device time of each stage in milliseconds to stage_ms[0..3]
- * (chunk_cumsum, chunk_state, state_passing, chunk_scan), measured with HIP
- * events recorded on `stream` between the launches.  For measurement only:
+ * (chunk_cumsum, chunk_state, state_passing, chunk_scan; on the span path
+ * the second and third are the span-end kernel and the jump across spans
+ * plus the replay), measured with HIP events recorded on `stream` between
+ * the launches.  For measurement only:
  * it creates and destroys five events and blocks the calling thread.
  */
 int mamba2_ssd_forward_profile(const mamba2_dims* dims, const void* x, const void* dt,

@@ -143,6 +143,23 @@ int enqueue_forward(const m2::Dims& d, const void* x, const void* dt, const floa
   if (e == hipSuccess) e = m2::launch_chunk_cumsum(d, dt, A, dA_cs, dt_T, s);
   if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
   if (ev) e = hipEventRecord(ev[1], s);
+  const int K = w.grouped ? m2::span_chunks(d) : 0;
+  const size_t span_bytes = K ? round256(m2::span_states_bytes(d, K)) : 0;
+  if (K && span_bytes + round256((size_t)(d.B * d.H * ((d.nc + K - 1) / K)) * 4) <= w.st_bytes) {
+    // fwd_pass_state over spans: span-end states (stage slot 1), then the
+    // jump across spans and the replay that writes the chunk-start states
+    // (stage slot 2)
+    float* span_decay = (float*)((char*)states + span_bytes);
+    if (e == hipSuccess)
+      e = m2::launch_fwd_pass_state_span(d, K, x, B, dA_cs, dt_T, init_state, states, span_decay,
+                                         hst, final_state, s, ev ? ev[2] : nullptr);
+    if (e != hipSuccess) return hip_status(e, "fwd_pass_state launch");
+    if (ev) e = hipEventRecord(ev[3], s);
+    if (e == hipSuccess) e = m2::launch_chunk_scan_grouped(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
+    if (e != hipSuccess) return hip_status(e, "chunk_scan launch");
+    if (ev) e = hipEventRecord(ev[4], s);
+    return hip_status(e, "event record");
+  }
   if (e == hipSuccess)
     e = m2::grouped_state_supported(d) ? m2::launch_chunk_state_grouped(d, x, B, dA_cs, dt_T, states, s)
                                        : m2::launch_chunk_state(d, x, B, dA_cs, dt_T, states, s);

@@ -68,6 +68,18 @@ hipError_t launch_bwd_param_sums(const Dims& d, const float* dA_part, const floa
 // fwd_pass_state as one kernel (bfloat16, P = 64, N in {64, 128, 256},
 // Q in {64, 128, 256}): chunk-start states to hst (bf16 [B,nc,H,P,N]) and the
 // final state, from the weights w_T = 2^(cs_last - cs_j) dt_j [B,H,nc,Q].
+// fwd_pass_state over spans of chunks (state_span.hip): span_chunks gives the
+// span length K (0 = this path does not apply to these sizes).  span_states
+// [B, ng, H, P, N] float32 and span_decay [B, H, ng] are scratch
+// (ng = ceil(nc / K)); hst receives the bfloat16 chunk-start states.  `mid`
+// (may be null) is recorded after the span-end kernel.
+int span_chunks(const Dims& d);
+size_t span_states_bytes(const Dims& d, int K);
+hipError_t launch_fwd_pass_state_span(const Dims& d, int K, const void* x, const void* B,
+                                      const float* dA_cs, const float* dt_T, const float* init,
+                                      float* span_states, float* span_decay, void* hst,
+                                      float* final_state, hipStream_t s, hipEvent_t mid);
+
 bool fused_state_supported(const Dims& d);
 hipError_t launch_chunk_weights(const Dims& d, const float* dA_cs, const float* dt_T, float* w_T,
                                 hipStream_t s);

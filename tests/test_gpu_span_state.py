@@ -1,0 +1,106 @@
+"""Parity of the forward's span path with the oracle.
+
+For bfloat16 with headdim 64, state size 64, 128 or 256 and enough
+(batch, head, span) work to give every CU a workgroup, mamba2_ssd_forward
+runs fwd_pass_state over spans of K = 8 (else 4) chunks: span-end states,
+the jump across spans, and a replay of every span that writes the chunk-start
+states, with 1, 2 or 4 heads of a group per workgroup.  These shapes meet
+that rule (checked below with the device's CU count) and cover every (chunk
+size, state size) pair, 1, 2 and 4 heads per workgroup, ragged last chunks, a
+last span of one chunk, several groups and batches, with and without the
+initial state.  y and the final state are compared with the oracle at the
+bfloat16 bar (2e-2 normwise); the full-size workload (L = 64K, N = 256,
+spans of 8) is covered on sampled heads by the full-size tests."""
+import pytest
+import torch
+
+import oracle
+import ssd_inputs
+from gpu_helpers import TOL, f64, normwise, oracle_inputs, run_forward, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+BT = TOL["bf16"]
+
+
+@pytest.fixture(scope="module")
+def m2():
+    import state_space_sequence_02_amd as lib
+    return lib
+
+
+def _w(name, L, H, N, G, Q, Bn=1, init=True, seed=0):
+    return ssd_inputs.custom(name=name, batch=Bn, seqlen=L, nheads=H, headdim=64, dstate=N,
+                             ngroups=G, chunk_size=Q, init_state=init, seed=seed)
+
+
+SHAPES = [
+    _w("span_Q64_N64_G2_K4", 1000, 64, 64, 2, 64, seed=91),
+    _w("span_Q64_N256_K8_last_span_one_chunk", 2085, 32, 256, 1, 64, Bn=2, seed=92),
+    _w("span_Q128_N128_G3_K4", 5115, 48, 128, 3, 128, init=False, seed=93),
+    _w("span_Q256_N64_G4_ragged", 3996, 64, 64, 4, 256, seed=94),
+    _w("span_Q128_N256_B2_K4", 4097, 16, 256, 1, 128, Bn=2, seed=95),
+    _w("span_Q256_N128_K4", 4096, 64, 128, 2, 256, init=False, seed=96),
+    _w("span_Q64_N128_B4", 1024, 16, 128, 1, 64, Bn=4, seed=97),
+    _w("span_Q256_N256_K4", 4096, 64, 256, 1, 256, seed=98),
+    # several heads per workgroup (sharing the B rows)
+    _w("span_Q64_N256_R4_ragged", 8155, 64, 256, 1, 64, seed=99),
+    _w("span_Q128_N128_G2_R4", 8192, 64, 128, 2, 128, Bn=2, init=False, seed=100),
+    _w("span_Q256_N64_G4_R2", 8192, 32, 64, 4, 256, Bn=4, seed=101),
+]
+
+# (span length, heads per workgroup) each shape reaches on a 256-CU device
+EXPECT = {"span_Q64_N256_K8_last_span_one_chunk": (8, 1), "span_Q64_N256_R4_ragged": (8, 4),
+          "span_Q128_N128_G2_R4": (8, 4), "span_Q256_N64_G4_R2": (8, 2)}
+
+
+def span_chunks(w, cus):
+    """The span length the library picks for these sizes (0: no span path)."""
+    if not (w.dtype == "bf16" and w.headdim == 64 and w.dstate in (64, 128, 256)
+            and w.chunk_size in (64, 128, 256)):
+        return 0
+    nc = -(-w.seqlen // w.chunk_size)
+    for K in (8, 4):
+        if nc >= K and w.batch * w.nheads * (-(-nc // K)) >= cus:
+            return K
+    return 0
+
+
+def span_heads(w, K, cus):
+    """Heads per workgroup the library picks: 4, 2 or 1, a divisor of the
+    group's heads, while the grid still gives every CU a workgroup."""
+    nc = -(-w.seqlen // w.chunk_size)
+    ng = -(-nc // K)
+    for R in (4, 2):
+        if (w.nheads // w.ngroups) % R == 0 and w.batch * ng * w.nheads // R >= cus:
+            return R
+    return 1
+
+
+@pytest.mark.parametrize("w", SHAPES, ids=lambda w: w.name)
+def test_span_forward_matches_oracle(m2, w):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    K = span_chunks(w, cus)
+    R = span_heads(w, K, cus) if K else 0
+    say(f"[span] {w} K={K} R={R}")
+    assert K > 0, "shape does not reach the span path on this device"
+    if cus == 256 and w.name in EXPECT:
+        assert (K, R) == EXPECT[w.name]
+    inp = ssd_inputs.make_inputs(w)
+    o = oracle_inputs(inp)
+    g = to_gpu(inp)
+    y, fin = run_forward(m2, g, w.chunk_size)
+    oy, ofin, _ = oracle.ssd_recurrence(o["x"], o["dt"], o["A"], o["B"], o["C"], o["D"],
+                                        o["init_state"], chunk_size=w.chunk_size)
+    ey, ef = normwise(f64(y), oy), normwise(f64(fin), ofin)
+    say(f"  y {ey:.3e} final {ef:.3e}")
+    assert ey <= BT
+    assert ef <= BT
+
+
+def test_span_forward_is_deterministic(m2):
+    w = SHAPES[1]
+    g = to_gpu(ssd_inputs.make_inputs(w))
+    y1, f1 = run_forward(m2, g, w.chunk_size)
+    y2, f2 = run_forward(m2, g, w.chunk_size)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
