@@ -108,25 +108,37 @@ __device__ __forceinline__ void load_head(uint32_t buf, const bf16* __restrict__
 }
 
 
+// Two floats to two bfloat16 (round to nearest even) in one conversion.
+typedef float cs_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 cs_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ cs_bf16x2 pk2(float a, float b) {
+  return __builtin_convertvector((cs_f32x2){a, b}, cs_bf16x2);
+}
+__device__ __forceinline__ bf16x4 pk4(float a, float b, float c, float d) {
+  return __builtin_shufflevector(pk2(a, b), pk2(c, d), 0, 1, 2, 3);
+}
+
 // Four elements (rows j = j0 + r) of the masked, decayed in-chunk weights of
 // column i: G^T * 2^(cs_i - cs_j) * dt_j, with lw_j = cs_j - log2(dt_j)
 // (dt_j = 0 gives +inf and weight 0).  Tiles strictly below the diagonal need
 // no mask; the diagonal tile is masked causally and carries the skip term D
 // on j == i, where the decay is 1.
-__device__ __forceinline__ void weights4(bf16x8& gm, int half, const f32x4 gt, const f32x4 lw,
-                                         float csi, bool diag, int j0, int i, float Dh) {
+__device__ __forceinline__ bf16x4 weights4(const f32x4 gt, const f32x4 lw, float csi, bool diag,
+                                           int j0, int i, float Dh) {
+  float v[4];
   if (!diag) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) gm[half * 4 + r] = f2bf(gt[r] * fast_exp2(csi - lw[r]));
+    for (int r = 0; r < 4; ++r) v[r] = gt[r] * fast_exp2(csi - lw[r]);
   } else {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = j0 + r;
       float gv = (j <= i) ? gt[r] * fast_exp2(csi - lw[r]) : 0.f;
       if (j == i) gv += Dh;
-      gm[half * 4 + r] = f2bf(gv);
+      v[r] = gv;
     }
   }
+  return pk4(v[0], v[1], v[2], v[3]);
 }
 
 // In-chunk contribution for both of a wave's i-tiles (t0 < t1): scales the
@@ -152,43 +164,47 @@ __device__ __forceinline__ void in_chunk(const f32x4 (&Gs)[QT + 1], f32x4 (&Y0)[
     Y0[pt] *= sc0;
     Y1[pt] *= sc1;
   }
+  // Byte offsets of the lane's transposed x reads inside a 32-row block: the
+  // swizzle of row 32 jp + r equals that of row r (it uses bits 1..3 of the
+  // row), so block jp is these offsets plus a constant jp * 32 rows.
+  const unsigned char* xa[PT][2];
+#pragma unroll
+  for (int pt = 0; pt < PT; ++pt) {
+    const int ra = 4 * grp + (L16 >> 2), rb = ra + 16;
+    const int p0 = 4 * PT * (L16 & 3) + 4 * pt;
+    const int ch = p0 >> 3, off = (p0 & 7) * 2;
+    xa[pt][0] = Xs + ra * (P * 2) + (xswz(ra, ch) << 4) + off;
+    xa[pt][1] = Xs + rb * (P * 2) + (xswz(rb, ch) << 4) + off;
+  }
 #pragma unroll
   for (int jp = 0; jp < QT / 2; ++jp) {
     if (2 * jp > t1) break;
     const int ja = 2 * jp, jb = 2 * jp + 1;
-    const int ra = 32 * jp + 4 * grp + (L16 >> 2), rb = ra + 16;
     bf16x8 xop[PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
-      const int p0 = 4 * PT * (L16 & 3) + 4 * pt;
-      const int ch = p0 >> 3, off = (p0 & 7) * 2;
-      const bf16* pa = (const bf16*)(Xs + ra * (P * 2) + (xswz(ra, ch) << 4) + off);
-      const bf16* pb = (const bf16*)(Xs + rb * (P * 2) + (xswz(rb, ch) << 4) + off);
+      const bf16* pa = (const bf16*)(xa[pt][0] + jp * 32 * (P * 2));
+      const bf16* pb = (const bf16*)(xa[pt][1] + jp * 32 * (P * 2));
       xop[pt] = cat(lds_read_tr(pa), lds_read_tr(pb));
     }
     const f32x4 lwa = *(const f32x4*)(lws + 16 * ja + 4 * grp);
     const f32x4 lwb = *(const f32x4*)(lws + 16 * jb + 4 * grp);
+    const bf16x4 zero4 = pk4(0.f, 0.f, 0.f, 0.f);
     {  // tile t1 (2 jp <= t1 here)
-      bf16x8 gm;
-      weights4(gm, 0, Gs[QT - ja], lwa, cs1, ja == t1, 16 * ja + 4 * grp, i1, Dh);
-      if (jb <= t1) {
-        weights4(gm, 1, Gs[QT - jb], lwb, cs1, jb == t1, 16 * jb + 4 * grp, i1, Dh);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gm[4 + r] = f2bf(0.f);
-      }
+      const bf16x4 lo = weights4(Gs[QT - ja], lwa, cs1, ja == t1, 16 * ja + 4 * grp, i1, Dh);
+      const bf16x4 hi = jb <= t1
+          ? weights4(Gs[QT - jb], lwb, cs1, jb == t1, 16 * jb + 4 * grp, i1, Dh) : zero4;
+      const bf16x8 gm = cat(lo, hi);
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) Y1[pt] = mfma16x16x32(xop[pt], gm, Y1[pt]);
     }
     if (ja < QT / 2 && ja <= t0) {  // tile t0
-      bf16x8 gm;
-      weights4(gm, 0, Gs[ja < QT / 2 ? ja : 0], lwa, cs0, ja == t0, 16 * ja + 4 * grp, i0, Dh);
-      if (jb < QT / 2 && jb <= t0) {
-        weights4(gm, 1, Gs[jb < QT / 2 ? jb : 0], lwb, cs0, jb == t0, 16 * jb + 4 * grp, i0, Dh);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gm[4 + r] = f2bf(0.f);
-      }
+      const bf16x4 lo = weights4(Gs[ja < QT / 2 ? ja : 0], lwa, cs0, ja == t0,
+                                 16 * ja + 4 * grp, i0, Dh);
+      const bf16x4 hi = (jb < QT / 2 && jb <= t0)
+          ? weights4(Gs[jb < QT / 2 ? jb : 0], lwb, cs0, jb == t0, 16 * jb + 4 * grp, i0, Dh)
+          : zero4;
+      const bf16x8 gm = cat(lo, hi);
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) Y0[pt] = mfma16x16x32(xop[pt], gm, Y0[pt]);
     }
@@ -207,12 +223,8 @@ __device__ __forceinline__ void store_tile(const f32x4 (&Yt)[P / 16], int t, bf1
     bf16* dst = y + (ybase + (int64_t)i * H) * P + 4 * PT * grp;
 #pragma unroll
     for (int pt = 0; pt < PT; pt += 2) {
-      bf16x8 o;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        o[r] = f2bf(Yt[pt][r]);
-        o[4 + r] = f2bf(Yt[pt + 1][r]);
-      }
+      const bf16x8 o = cat(pk4(Yt[pt][0], Yt[pt][1], Yt[pt][2], Yt[pt][3]),
+                           pk4(Yt[pt + 1][0], Yt[pt + 1][1], Yt[pt + 1][2], Yt[pt + 1][3]));
       *(bf16x8*)(dst + 4 * pt) = o;
     }
   }
