@@ -232,20 +232,36 @@ struct DmaPlan {
   }
 };
 
+// Which part of the run's states tile m of wave w holds: R tiles of 32 state
+// columns each (all 64 rows as 2 x 4 MFMA tiles).  With R <= NW the NW / R
+// waves of a head split its N columns, so a wave contracts one head's x rows;
+// with more heads than waves (N = 64), a wave holds R / NW heads whole.
+template <int NW, int R>
+__device__ __forceinline__ int tile_head(int w, int m) {
+  return NW >= R ? w / (NW / R) : w * (R / NW) + m / NW;
+}
+template <int NW, int R>
+__device__ __forceinline__ int tile_cols(int w, int m) {  // 32-column group
+  return NW >= R ? (w % (NW / R)) * R + m : m % NW;
+}
+
 template <int Q, int N, int R>
 __device__ __forceinline__ void store_hst(bf16* __restrict__ hst, const f32x4 (&acc)[R][2][4],
                                           int b, int c, int h0, int H, int nc, int L16,
-                                          int ncol) {
+                                          int grp, int w) {
+  using C = SpanCfg<Q, N, R>;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int m = 0; m < R; ++m) {
+    const int r = tile_head<C::NW, R>(w, m);
+    const int ncol = 32 * tile_cols<C::NW, R>(w, m) + 8 * grp;
     bf16* dst = hst + ((((int64_t)b * nc + c) * H + h0 + r) * 64 + L16) * N + ncol;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       bf16x8 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        o[e] = f2bf(acc[r][0][pt][e]);
-        o[4 + e] = f2bf(acc[r][1][pt][e]);
+        o[e] = f2bf(acc[m][0][pt][e]);
+        o[4 + e] = f2bf(acc[m][1][pt][e]);
       }
       *(bf16x8*)(dst + (int64_t)16 * pt * N) = o;
     }
@@ -279,25 +295,27 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R>::NT), (SpanCfg<Q, N, R>::WPE
   const int lane = lane_id();
   const int w = wave_id();
   const int L16 = lane & 15, grp = lane >> 4;
-  const int ncol = 32 * w + 8 * grp;  // first of this lane's 8 state columns
   // this wave's direct-to-LDS loads per block
   const int nw = C::TOT / C::NW + (w < C::TOT % C::NW ? 1 : 0);
 
-  // acc[r][nt][pt][e] = state of head h0 + r at [p = 16 pt + L16][n = ncol + 4 nt + e]
+  // acc[m][nt][pt][e] = state of head h0 + tile_head(w, m) at
+  // [p = 16 pt + L16][n = 32 tile_cols(w, m) + 8 grp + 4 nt + e]
   f32x4 acc[R][2][4];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int m = 0; m < R; ++m) {
+    const int r = tile_head<C::NW, R>(w, m);
+    const int ncol = 32 * tile_cols<C::NW, R>(w, m) + 8 * grp;
     const float* sst = span_states + (((int64_t)b * ng + s) * H + h0 + r) * 64 * N;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        acc[r][nt][pt] = REPLAY ? *(const f32x4*)(sst + (16 * pt + L16) * N + ncol + 4 * nt)
+        acc[m][nt][pt] = REPLAY ? *(const f32x4*)(sst + (16 * pt + L16) * N + ncol + 4 * nt)
                                 : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float dsum[R], csl[R];
+  float dsum[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) dsum[r] = csl[r] = 0.f;
+  for (int r = 0; r < R; ++r) dsum[r] = 0.f;
 
   const uint32_t sbase = lds_addr(smem);
   __builtin_amdgcn_s_waitcnt(0);  // the start states are in registers
@@ -341,17 +359,16 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R>::NT), (SpanCfg<Q, N, R>::WPE
     const float* cl = (const float*)(cur + C::XS + C::BS + C::CS);
     if (jb == 0) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) csl[r] = cl[4 * r + 3];
-      if (REPLAY) store_hst<Q, N, R>(hst, acc, b, c, h0, H, nc, L16, ncol);
+      for (int r = 0; r < R; ++r) dsum[r] += cl[4 * r + 3];
+      if (REPLAY) store_hst<Q, N, R>(hst, acc, b, c, h0, H, nc, L16, grp, w);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float dec = fast_exp2(csl[r]);
+      for (int m = 0; m < R; ++m) {
+        const float dec = fast_exp2(cl[4 * tile_head<C::NW, R>(w, m) + 3]);
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-          acc[r][0][pt] *= dec;
-          acc[r][1][pt] *= dec;
+          acc[m][0][pt] *= dec;
+          acc[m][1][pt] *= dec;
         }
-        dsum[r] += csl[r];
       }
     }
     // scale the x rows by w_j in place: slot s is head s / 256, row (s % 256) / 8
@@ -371,17 +388,10 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R>::NT), (SpanCfg<Q, N, R>::WPE
     lds_barrier();
     const unsigned char* bsm = cur + C::XS;
     const int ra = 8 * grp + (L16 >> 2), rb = ra + 4;
-    const int bc = 4 * w + (L16 & 3);
-    bf16x8 bop[2];
+    constexpr int HPW = R > C::NW ? R / C::NW : 1;  // heads per wave
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const bf16* pa = (const bf16*)(bsm + ra * (2 * N) + sb<N>(ra, bc) * 16 + 8 * nt);
-      const bf16* pb = (const bf16*)(bsm + rb * (2 * N) + sb<N>(rb, bc) * 16 + 8 * nt);
-      bop[nt] = cat(lds_read_tr(pa), lds_read_tr(pb));
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const unsigned char* xs = cur + r * C::XH;
+    for (int hh = 0; hh < HPW; ++hh) {
+      const unsigned char* xs = cur + tile_head<C::NW, R>(w, hh * (R / HPW)) * C::XH;
       bf16x8 xop[4];
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
@@ -391,26 +401,42 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R>::NT), (SpanCfg<Q, N, R>::WPE
         xop[pt] = cat(lds_read_tr(pa), lds_read_tr(pb));
       }
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int v = 0; v < R / HPW; ++v) {
+        const int m = hh * (R / HPW) + v;
+        const int bc = 4 * tile_cols<C::NW, R>(w, m) + (L16 & 3);
+        bf16x8 bop[2];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-          acc[r][nt][pt] = mfma16x16x32(bop[nt], xop[pt], acc[r][nt][pt]);
+        for (int nt = 0; nt < 2; ++nt) {
+          const bf16* pa = (const bf16*)(bsm + ra * (2 * N) + sb<N>(ra, bc) * 16 + 8 * nt);
+          const bf16* pb = (const bf16*)(bsm + rb * (2 * N) + sb<N>(rb, bc) * 16 + 8 * nt);
+          bop[nt] = cat(lds_read_tr(pa), lds_read_tr(pb));
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt)
+            acc[m][nt][pt] = mfma16x16x32(bop[nt], xop[pt], acc[m][nt][pt]);
+      }
     }
   }
 
   if (REPLAY) {  // start state of the span's last chunk
-    store_hst<Q, N, R>(hst, acc, b, c1 - 1, h0, H, nc, L16, ncol);
+    store_hst<Q, N, R>(hst, acc, b, c1 - 1, h0, H, nc, L16, grp, w);
   } else {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int m = 0; m < R; ++m) {
+      const int r = tile_head<C::NW, R>(w, m);
+      const int ncol = 32 * tile_cols<C::NW, R>(w, m) + 8 * grp;
       float* sst = span_states + (((int64_t)b * ng + s) * H + h0 + r) * 64 * N;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          *(f32x4*)(sst + (16 * pt + L16) * N + ncol + 4 * nt) = acc[r][nt][pt];
-      if (tid == 0) span_decay[((int64_t)b * H + h0 + r) * ng + s] = dsum[r];
+          *(f32x4*)(sst + (16 * pt + L16) * N + ncol + 4 * nt) = acc[m][nt][pt];
     }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (tid == 0) span_decay[((int64_t)b * H + h0 + r) * ng + s] = dsum[r];
   }
 }
 

@@ -47,11 +47,14 @@ SHAPES = [
     _w("span_Q64_N256_R4_ragged", 8155, 64, 256, 1, 64, seed=99),
     _w("span_Q128_N128_G2_R4", 8192, 64, 128, 2, 128, Bn=2, init=False, seed=100),
     _w("span_Q256_N64_G4_R2", 8192, 32, 64, 4, 256, Bn=4, seed=101),
+    # N = 64 with 4 heads per workgroup: two heads per wave
+    _w("span_Q64_N64_R4_ragged", 2000, 64, 64, 1, 64, Bn=4, seed=102),
 ]
 
 # (span length, heads per workgroup) each shape reaches on a 256-CU device
 EXPECT = {"span_Q64_N256_K8_last_span_one_chunk": (8, 1), "span_Q64_N256_R4_ragged": (8, 4),
-          "span_Q128_N128_G2_R4": (8, 4), "span_Q256_N64_G4_R2": (8, 2)}
+          "span_Q128_N128_G2_R4": (8, 4), "span_Q256_N64_G4_R2": (8, 2),
+          "span_Q64_N64_R4_ragged": (8, 4)}
 
 
 def span_chunks(w, cus):
