@@ -7,7 +7,7 @@ Prints one JSON line with tokens/s, the roofline position of the dominant
 kernel (per-kernel durations measured here with HIP events on the launch
 stream) and the CPU oracle's throughput on the host as a reported baseline.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload long_L64k_N256]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 100] [--workload long_L64k_N256]
     python bench.py --backward      (the backward pass on the same workload)
     python bench.py --decode-batch B (the one-token recurrent step)
 """
@@ -106,8 +106,8 @@ def stage_model(w, cus=256):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="long_L64k_N256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
