@@ -33,7 +33,7 @@ STAGES = ("chunk_cumsum", "chunk_state", "state_passing", "chunk_scan")
 def grouped_path(w):
     """The fused forward hands the chunk-start states to the output stage as
     bfloat16 for these sizes (same rule as the library's dispatch)."""
-    return (w.dtype == "bf16" and w.headdim == 64 and w.dstate in (64, 128, 256)
+    return (w.dtype == "bf16" and w.headdim == 64 and w.dstate in (64, 128, 256, 512)
             and w.chunk_size in (64, 128, 256))
 
 
@@ -42,7 +42,7 @@ def span_plan(w, cus=256):
     None where the library runs chunk_state + state_passing (same rule as
     the library's dispatch: spans of 8, else 4, chunks while the grid gives
     every CU a workgroup; R = 4, 2 or 1 heads of a group likewise)."""
-    if not grouped_path(w):
+    if not grouped_path(w) or w.dstate == 512:
         return None
     nc = w.nchunks
     for K in (8, 4):
@@ -119,11 +119,17 @@ def main():
                          "(H=32, P=64, N=256, bf16)")
     ap.add_argument("--backward", action="store_true",
                     help="only measure the backward pass (mamba2_ssd_backward) on the workload")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only measure the forward over sequence lengths 1K-256K and state "
+                         "sizes 64-512 (H=32, P=64, G=1, Q=256, bf16): one JSON line per shape")
     ap.add_argument("--state-path", choices=("default", "fused"), default="default",
                     help="fused: measure mamba2_ssd_forward_fused (one-kernel fwd_pass_state)")
     args = ap.parse_args()
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.sweep:
+        sweep_bench(args)
         return
     if args.decode_batch:
         decode_bench(args)
@@ -381,6 +387,88 @@ def profiled_traffic(workload, stage, direction="forward"):
             except ValueError:
                 return None
     return None
+
+
+SWEEP_L = (1024, 4096, 16384, 65536, 262144)
+SWEEP_N = (64, 128, 256, 512)
+
+
+def sweep_bench(args):
+    """Forward throughput over the pages' sweep of sequence lengths and state
+    sizes (1K-256K tokens, N = 64-512): batch 1, 32 heads of 64, one B/C
+    group, chunk 256, bf16, inputs resident.  Each shape is warmed up for at
+    least 0.3 s of back-to-back steps (clocks settle) and then timed over at
+    least 100 steps and 0.2 s with HIP events on the launch stream.  The
+    roofline fraction is the path's algorithmic HBM bytes (the stages the
+    library runs for that shape, as in stage_model) over the step time,
+    against 8 TB/s; MFMA is the algorithmic flops over the step time against
+    the dense bf16 peak."""
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import ssd_inputs
+    import state_space_sequence_02_amd as m2
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream()
+    for N in SWEEP_N:
+        for L in SWEEP_L:
+            w = ssd_inputs.custom(name=f"sweep_L{L // 1024}k_N{N}", batch=1, seqlen=L, nheads=32,
+                                  headdim=64, dstate=N, ngroups=1, chunk_size=256,
+                                  dtype="bf16", init_state=False, seed=2000 + N + L // 1024)
+            g = {k: (None if v is None else v.to(dev))
+                 for k, v in ssd_inputs.make_inputs(w).items()}
+            dims = m2.dims_of(g["x"], g["B"], w.chunk_size)
+            y = torch.empty_like(g["x"])
+            fin = torch.empty((1, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+            need = m2.mamba2_ssd_workspace_bytes(dims)
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+            def step():
+                m2.mamba2_ssd_forward(dims, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"],
+                                      g["init_state"], y, fin, ws, need, stream)
+
+            t_end = time.perf_counter() + 0.3
+            while time.perf_counter() < t_end:
+                for _ in range(10):
+                    step()
+                torch.cuda.synchronize()
+            step()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            n = 0
+            while n < 100 or time.perf_counter() - t0 < 0.2:
+                step()
+                n += 1
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n
+            model = stage_model(w, cus)
+            names = forward_stages(w, cus)
+            byt = sum(model[s]["bytes"] for s in names)
+            flo = sum(model[s]["flops"] for s in names)
+            plan = span_plan(w, cus)
+            path = (f"span K={plan[0]} R={plan[1]}" if plan else
+                    ("split, bf16 start states" if grouped_path(w) else "split, per head"))
+            print(json.dumps({
+                "workload": w.name, "seqlen": L, "dstate": N, "nheads": w.nheads,
+                "headdim": w.headdim, "ngroups": w.ngroups, "chunk_size": w.chunk_size,
+                "path": path, "steps": n, "ms_per_step": round(ms, 4),
+                "tokens_per_s": L / (ms * 1e-3),
+                "algorithmic_bytes": byt, "GB/s": round(byt / (ms * 1e-3) / 1e9, 1),
+                "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+                "TFLOP/s": round(flo / (ms * 1e-3) / 1e12, 1),
+                "mfma_frac": round(flo / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 3)}),
+                flush=True)
+            del g, y, fin, ws
+            torch.cuda.empty_cache()
 
 
 def copy_probe(mib):

@@ -111,10 +111,11 @@ int hip_status(hipError_t e, const char* where) {
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Workspace of the fused forward: dA_cs and dt_T [B,H,nc,Q] f32, the per-chunk
-// states [B,nc,H,P,N] f32, and (grouped path) the chunk-start states as bf16.
+// states [B,nc,H,P,N] f32, (grouped path) the chunk-start states as bf16, and
+// (grouped path at state size 512) the first column half's float32 y.
 struct Workspace {
   bool grouped;
-  size_t cs_bytes, st_bytes, hst_bytes, total;
+  size_t cs_bytes, st_bytes, hst_bytes, part_bytes, total;
 };
 
 Workspace plan(const m2::Dims& d) {
@@ -123,7 +124,8 @@ Workspace plan(const m2::Dims& d) {
   w.cs_bytes = round256((size_t)(d.B * d.H * d.nc * d.Q) * sizeof(float));
   w.st_bytes = round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * sizeof(float));
   w.hst_bytes = w.grouped ? round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * 2) : 0;
-  w.total = 2 * w.cs_bytes + w.st_bytes + w.hst_bytes;
+  w.part_bytes = w.grouped ? round256(m2::grouped_scan_part_bytes(d)) : 0;
+  w.total = 2 * w.cs_bytes + w.st_bytes + w.hst_bytes + w.part_bytes;
   return w;
 }
 
@@ -138,6 +140,7 @@ int enqueue_forward(const m2::Dims& d, const void* x, const void* dt, const floa
   float* dt_T = (float*)(ws + w.cs_bytes);
   float* states = (float*)(ws + 2 * w.cs_bytes);
   void* hst = ws + 2 * w.cs_bytes + w.st_bytes;
+  float* part = w.part_bytes ? (float*)(ws + 2 * w.cs_bytes + w.st_bytes + w.hst_bytes) : nullptr;
   hipError_t e = hipSuccess;
   if (ev) e = hipEventRecord(ev[0], s);
   if (e == hipSuccess) e = m2::launch_chunk_cumsum(d, dt, A, dA_cs, dt_T, s);
@@ -155,7 +158,8 @@ int enqueue_forward(const m2::Dims& d, const void* x, const void* dt, const floa
                                          hst, final_state, s, ev ? ev[2] : nullptr);
     if (e != hipSuccess) return hip_status(e, "fwd_pass_state launch");
     if (ev) e = hipEventRecord(ev[3], s);
-    if (e == hipSuccess) e = m2::launch_chunk_scan_grouped(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
+    if (e == hipSuccess)
+      e = m2::launch_chunk_scan_grouped(d, x, B, C, dA_cs, dt_T, hst, D, y, part, s);
     if (e != hipSuccess) return hip_status(e, "chunk_scan launch");
     if (ev) e = hipEventRecord(ev[4], s);
     return hip_status(e, "event record");
@@ -171,7 +175,7 @@ int enqueue_forward(const m2::Dims& d, const void* x, const void* dt, const floa
   if (e != hipSuccess) return hip_status(e, "state_passing launch");
   if (ev) e = hipEventRecord(ev[3], s);
   if (e == hipSuccess)
-    e = w.grouped ? m2::launch_chunk_scan_grouped(d, x, B, C, dA_cs, dt_T, hst, D, y, s)
+    e = w.grouped ? m2::launch_chunk_scan_grouped(d, x, B, C, dA_cs, dt_T, hst, D, y, part, s)
                   : m2::launch_chunk_scan(d, x, B, C, dA_cs, dt_T, states, D, y, s);
   if (e != hipSuccess) return hip_status(e, "chunk_scan launch");
   if (ev) e = hipEventRecord(ev[4], s);
@@ -399,7 +403,8 @@ int mamba2_ssd_forward_fused(const mamba2_dims* dims, const void* x, const void*
   if (e == hipSuccess) e = m2::launch_chunk_weights(d, dA_cs, dt_T, w_T, s);
   if (e == hipSuccess)
     e = m2::launch_fwd_pass_state(d, x, B, dA_cs, w_T, init_state, hst, final_state, s);
-  if (e == hipSuccess) e = m2::launch_chunk_scan_grouped(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
+  if (e == hipSuccess)
+    e = m2::launch_chunk_scan_grouped(d, x, B, C, dA_cs, dt_T, hst, D, y, nullptr, s);
   return hip_status(e, "ssd_forward_fused launch");
 }
 

@@ -36,6 +36,8 @@ namespace {
 #endif
 constexpr int kHopAhead = M2_HOP_AHEAD;  // state-operand reads in flight ahead of the MFMAs
 
+enum ScanMode { kWhole = 0, kFirstHalf = 1, kSecondHalf = 2 };
+
 template <int P, int Q, int N>
 struct GCfg {
   static constexpr int QT = Q / 16, NW = Q / 32, PT = P / 16, NBLK = N / 64;
@@ -66,17 +68,19 @@ __device__ __forceinline__ int xswz(int r, int c) { return c ^ ((r >> 1) & 7); }
 // Issues the direct-to-LDS loads of one head into buffer `buf`:
 // state rows (P x N bf16), x rows (Q x P bf16, rows past L clamped to L-1,
 // whose values are never used with a nonzero weight), cumulative sums, dt.
-template <int P, int Q, int N>
+// In the second half pass only the state columns and the sums are needed.
+// The state rows are `ldn` elements long; this pass reads columns n0 .. n0 + N - 1.
+template <int P, int Q, int N, int MODE>
 __device__ __forceinline__ void load_head(uint32_t buf, const bf16* __restrict__ hst,
                                           const bf16* __restrict__ x,
                                           const float* __restrict__ dA_cs,
                                           const float* __restrict__ dt_T, int b, int c, int h,
-                                          int L, int H, int nc) {
+                                          int L, int H, int nc, int ldn, int n0) {
   using K = GCfg<P, Q, N>;
   const int lane = lane_id();
   const int w = wave_id();
   // state: P*N/512 wave-loads of 64 chunks
-  const bf16* hsrc = hst + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+  const bf16* hsrc = hst + (((int64_t)b * nc + c) * H + h) * (int64_t)P * ldn + n0;
   constexpr int HI = P * N / 512 / K::NW;
 #pragma unroll
   for (int i = 0; i < HI; ++i) {
@@ -84,7 +88,13 @@ __device__ __forceinline__ void load_head(uint32_t buf, const bf16* __restrict__
     const int s = k * 64 + lane;
     const int r = s / K::RLH, pos = s % K::RLH;
     const int cc = hswz<K::RLH>(r, pos);  // involution: position <-> chunk
-    dma16(hsrc + r * N + cc * 8, buf + k * 1024);
+    dma16(hsrc + (int64_t)r * ldn + cc * 8, buf + k * 1024);
+  }
+  const uint32_t cs = buf + K::HS_BYTES + K::XS_BYTES;
+  const int64_t cb = (((int64_t)b * H + h) * nc + c) * Q;
+  if (MODE == kSecondHalf) {  // cumulative sums only (wave 0)
+    if (w == 0 && lane < Q / 4) dma16(dA_cs + cb + lane * 4, cs);
+    return;
   }
   // x rows: Q/8 wave-loads of 8 rows
   const uint32_t xs = buf + K::HS_BYTES;
@@ -99,8 +109,6 @@ __device__ __forceinline__ void load_head(uint32_t buf, const bf16* __restrict__
     dma16(x + (((int64_t)b * L + t) * H + h) * P + xswz(r, pos) * 8, xs + k * 1024);
   }
   // cumulative sums (wave 0) and dt (wave 1): Q/4 chunks each
-  const uint32_t cs = xs + K::XS_BYTES;
-  const int64_t cb = (((int64_t)b * H + h) * nc + c) * Q;
   if (w < 2 && lane < Q / 4) {
     const float* src = (w == 0 ? dA_cs : dt_T) + cb + lane * 4;
     dma16(src, cs + w * K::CS_BYTES);
@@ -230,14 +238,53 @@ __device__ __forceinline__ void store_tile(const f32x4 (&Yt)[P / 16], int t, bf1
   }
 }
 
-template <int P, int Q, int N>
+// The first half pass's float32 y: the same lane layout as store_tile,
+// 4 PT consecutive p of one token per lane (4 PT * 4 bytes, 16-byte stores),
+// in a [B, L, H, P] float32 buffer.
+template <int P>
+__device__ __forceinline__ void store_part(const f32x4 (&Yt)[P / 16], int t,
+                                           float* __restrict__ part, int64_t ybase, int H,
+                                           int64_t valid) {
+  constexpr int PT = P / 16;
+  const int lane = lane_id();
+  const int L16 = lane & 15, grp = lane >> 4;
+  const int i = 16 * t + L16;
+  if (i < valid) {
+    float* dst = part + (ybase + (int64_t)i * H) * P + 4 * PT * grp;
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) *(f32x4*)(dst + 4 * pt) = Yt[pt];
+  }
+}
+
+// Adds the first half pass's float32 y to one i-tile (rows past the
+// sequence end are neither read nor stored).
+template <int P>
+__device__ __forceinline__ void add_part(f32x4 (&Yt)[P / 16], int t,
+                                         const float* __restrict__ part, int64_t ybase, int H,
+                                         int64_t valid) {
+  constexpr int PT = P / 16;
+  const int lane = lane_id();
+  const int L16 = lane & 15, grp = lane >> 4;
+  const int i = 16 * t + L16;
+  if (i < valid) {
+    const float* src = part + (ybase + (int64_t)i * H) * P + 4 * PT * grp;
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) Yt[pt] += *(const f32x4*)(src + 4 * pt);
+  }
+}
+
+template <int P, int Q, int N, int MODE>
 __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
     const float* __restrict__ dA_cs, const float* __restrict__ dt_T,
-    const bf16* __restrict__ hst, const float* __restrict__ Dv, bf16* __restrict__ y, int L,
-    int H, int G, int nc, int hpw, int slices) {
+    const bf16* __restrict__ hst, const float* __restrict__ Dv, bf16* __restrict__ y,
+    float* __restrict__ part, int L, int H, int G, int nc, int hpw, int slices, int n0) {
   using K = GCfg<P, Q, N>;
   constexpr int QT = K::QT, PT = K::PT, NBLK = K::NBLK, SROW = K::SROW;
+  // rows of B, C and the start states hold ldn columns; G^T runs over all of
+  // them (GBLK blocks of 64), the carried-state term over N from n0
+  constexpr int ldn = MODE == kWhole ? N : 2 * N;
+  constexpr int GBLK = MODE == kSecondHalf ? 0 : ldn / 64;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   bf16* Cs = (bf16*)(smem + K::BUF);  // phase-A staging aliases buffer 1
   bf16* Bs = Cs + Q * SROW;
@@ -263,7 +310,7 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
 
   // Head 0's bytes start flowing while G is formed.
   const uint32_t sbase = lds_addr(smem);
-  load_head<P, Q, N>(sbase, hst, x, dA_cs, dt_T, b, c, h0, L, H, nc);
+  load_head<P, Q, N, MODE>(sbase, hst, x, dA_cs, dt_T, b, c, h0, L, H, nc, ldn, n0);
 
   // ---- Phase A: G^T tiles of this wave's two i-tiles, and its C operands.
   // G^T tiles: j-tile jt of i-tile t0 in slot jt (jt <= t0), of i-tile t1 in
@@ -272,23 +319,24 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
 #pragma unroll
   for (int a = 0; a <= QT; ++a) Gs[a] = f32x4{0.f, 0.f, 0.f, 0.f};
   bf16x8 C0[NBLK][2], C1[NBLK][2];
+  constexpr int ABLK = GBLK > NBLK ? GBLK : NBLK;  // 64-column blocks staged
 #pragma unroll
-  for (int nb = 0; nb < NBLK; ++nb) {
+  for (int nb = 0; nb < ABLK; ++nb) {
     lds_barrier();
     for (int idx = tid; idx < Q * 8; idx += nthr) {
       const int r = idx >> 3, c8 = (idx & 7) * 8;
       const int64_t t = tok0 + r;
       bf16x8 vc, vb;
       if (t < L) {
-        const int64_t off = (((int64_t)b * L + t) * G + g) * N + nb * 64 + c8;
+        const int64_t off = (((int64_t)b * L + t) * G + g) * ldn + n0 + nb * 64 + c8;
         vc = *(const bf16x8*)(Cm + off);
-        vb = *(const bf16x8*)(Bm + off);
+        if (nb < GBLK) vb = *(const bf16x8*)(Bm + off);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) vc[e] = vb[e] = f2bf(0.f);
       }
       *(bf16x8*)(Cs + r * SROW + c8) = vc;
-      *(bf16x8*)(Bs + r * SROW + c8) = vb;
+      if (nb < GBLK) *(bf16x8*)(Bs + r * SROW + c8) = vb;
     }
     lds_barrier();
 #pragma unroll
@@ -296,14 +344,18 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
       const int koff = kk * 32 + grp * 8;
       const bf16x8 c0 = *(const bf16x8*)(Cs + (16 * t0 + L16) * SROW + koff);
       const bf16x8 c1 = *(const bf16x8*)(Cs + (16 * t1 + L16) * SROW + koff);
-      C0[nb][kk] = c0;
-      C1[nb][kk] = c1;
+      if (nb < NBLK) {
+        C0[nb][kk] = c0;
+        C1[nb][kk] = c1;
+      }
+      if (nb < GBLK) {
 #pragma unroll
-      for (int jt = 0; jt < QT; ++jt) {
-        if (jt <= t1) {
-          const bf16x8 bop = *(const bf16x8*)(Bs + (16 * jt + L16) * SROW + koff);
-          if (jt < QT / 2 && jt <= t0) Gs[jt] = mfma16x16x32(bop, c0, Gs[jt]);
-          Gs[QT - jt] = mfma16x16x32(bop, c1, Gs[QT - jt]);
+        for (int jt = 0; jt < QT; ++jt) {
+          if (jt <= t1) {
+            const bf16x8 bop = *(const bf16x8*)(Bs + (16 * jt + L16) * SROW + koff);
+            if (jt < QT / 2 && jt <= t0) Gs[jt] = mfma16x16x32(bop, c0, Gs[jt]);
+            Gs[QT - jt] = mfma16x16x32(bop, c1, Gs[QT - jt]);
+          }
         }
       }
     }
@@ -316,7 +368,8 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
     const int h = h0 + k;
     unsigned char* cur = smem + (k & 1) * K::BUF;
     if (k + 1 < nh)
-      load_head<P, Q, N>(sbase + ((k + 1) & 1) * K::BUF, hst, x, dA_cs, dt_T, b, c, h + 1, L, H, nc);
+      load_head<P, Q, N, MODE>(sbase + ((k + 1) & 1) * K::BUF, hst, x, dA_cs, dt_T, b, c, h + 1,
+                               L, H, nc, ldn, n0);
     const unsigned char* Hs = cur;
     const unsigned char* Xs = cur + K::HS_BYTES;
     const float* css = (const float*)(Xs + K::XS_BYTES);
@@ -351,6 +404,25 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    const int64_t valid = L - tok0;
+    const int64_t ybase = ((int64_t)b * L + tok0) * H + h;
+    if (MODE == kSecondHalf) {
+      // carried-state term of the second half, scaled by 2^cs_i, plus the
+      // first pass's float32 y
+      const float sc0 = fast_exp2(css[16 * t0 + L16]), sc1 = fast_exp2(css[16 * t1 + L16]);
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        Y[0][pt] *= sc0;
+        Y[1][pt] *= sc1;
+      }
+      add_part<P>(Y[0], t0, part, ybase, H, valid);
+      add_part<P>(Y[1], t1, part, ybase, H, valid);
+      __builtin_amdgcn_s_waitcnt(0);  // next head's bytes have landed
+      store_tile<P>(Y[0], t0, y, ybase, H, valid);
+      store_tile<P>(Y[1], t1, y, ybase, H, valid);
+      lds_barrier();
+      continue;
+    }
     // dt_j -> cs_j - log2(dt_j), in place (the in-chunk weights' exponent offset)
     if (tid < Q) {
       float* lw = (float*)dts;
@@ -363,9 +435,13 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
     in_chunk<QT, P>(Gs, Y[0], Y[1], t0, t1, css, dts, Xs, Dh, l16, lgrp);
 
     __builtin_amdgcn_s_waitcnt(0);  // next head's bytes have landed (and older stores drained)
-    const int64_t valid = L - tok0;
-    store_tile<P>(Y[0], t0, y, ((int64_t)b * L + tok0) * H + h, H, valid);
-    store_tile<P>(Y[1], t1, y, ((int64_t)b * L + tok0) * H + h, H, valid);
+    if (MODE == kFirstHalf) {
+      store_part<P>(Y[0], t0, part, ybase, H, valid);
+      store_part<P>(Y[1], t1, part, ybase, H, valid);
+    } else {
+      store_tile<P>(Y[0], t0, y, ybase, H, valid);
+      store_tile<P>(Y[1], t1, y, ybase, H, valid);
+    }
     lds_barrier();
   }
 }
@@ -381,12 +457,12 @@ int cu_count() {
   return n;
 }
 
-template <int P, int Q, int N>
+template <int P, int Q, int N, int MODE>
 hipError_t launch_grouped(const Dims& d, const void* x, const void* B, const void* C,
                           const float* dA_cs, const float* dt_T, const void* hst, const float* D,
-                          void* y, hipStream_t s) {
+                          void* y, float* part, int n0, hipStream_t s) {
   using K = GCfg<P, Q, N>;
-  auto kern = chunk_scan_grouped_kernel<P, Q, N>;
+  auto kern = chunk_scan_grouped_kernel<P, Q, N, MODE>;
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS);
   if (attr != hipSuccess) return attr;
@@ -401,18 +477,26 @@ hipError_t launch_grouped(const Dims& d, const void* x, const void* B, const voi
   const int64_t grid = d.B * d.nc * d.G * slices;
   kern<<<(unsigned)grid, Q * 2, K::LDS, s>>>(
       (const bf16*)x, (const bf16*)B, (const bf16*)C, dA_cs, dt_T, (const bf16*)hst, D,
-      (bf16*)y, (int)d.L, (int)d.H, (int)d.G, (int)d.nc, (int)hpw, (int)slices);
+      (bf16*)y, part, (int)d.L, (int)d.H, (int)d.G, (int)d.nc, (int)hpw, (int)slices, n0);
   return hipGetLastError();
 }
 
 template <int Q>
 hipError_t launch_grouped_n(const Dims& d, const void* x, const void* B, const void* C,
                             const float* dA_cs, const float* dt_T, const void* hst,
-                            const float* D, void* y, hipStream_t s) {
+                            const float* D, void* y, float* part, hipStream_t s) {
   switch (d.N) {
-    case 64: return launch_grouped<64, Q, 64>(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
-    case 128: return launch_grouped<64, Q, 128>(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
-    case 256: return launch_grouped<64, Q, 256>(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
+    case 64: return launch_grouped<64, Q, 64, kWhole>(d, x, B, C, dA_cs, dt_T, hst, D, y, nullptr, 0, s);
+    case 128: return launch_grouped<64, Q, 128, kWhole>(d, x, B, C, dA_cs, dt_T, hst, D, y, nullptr, 0, s);
+    case 256: return launch_grouped<64, Q, 256, kWhole>(d, x, B, C, dA_cs, dt_T, hst, D, y, nullptr, 0, s);
+    case 512: {
+      if (!part) return hipErrorInvalidValue;
+      const hipError_t e = launch_grouped<64, Q, 256, kFirstHalf>(d, x, B, C, dA_cs, dt_T, hst,
+                                                                   D, y, part, 0, s);
+      if (e != hipSuccess) return e;
+      return launch_grouped<64, Q, 256, kSecondHalf>(d, x, B, C, dA_cs, dt_T, hst, D, y, part,
+                                                     256, s);
+    }
     default: return hipErrorInvalidValue;
   }
 }
@@ -420,17 +504,21 @@ hipError_t launch_grouped_n(const Dims& d, const void* x, const void* B, const v
 }  // namespace
 
 bool grouped_scan_supported(const Dims& d) {
-  return d.bf16 && d.P == 64 && (d.N == 64 || d.N == 128 || d.N == 256) &&
+  return d.bf16 && d.P == 64 && (d.N == 64 || d.N == 128 || d.N == 256 || d.N == 512) &&
          (d.Q == 64 || d.Q == 128 || d.Q == 256);
+}
+
+size_t grouped_scan_part_bytes(const Dims& d) {
+  return d.N == 512 ? (size_t)(d.B * d.L * d.H * d.P) * sizeof(float) : 0;
 }
 
 hipError_t launch_chunk_scan_grouped(const Dims& d, const void* x, const void* B, const void* C,
                                      const float* dA_cs, const float* dt_T, const void* hst,
-                                     const float* D, void* y, hipStream_t s) {
+                                     const float* D, void* y, float* part, hipStream_t s) {
   switch (d.Q) {
-    case 64: return launch_grouped_n<64>(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
-    case 128: return launch_grouped_n<128>(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
-    case 256: return launch_grouped_n<256>(d, x, B, C, dA_cs, dt_T, hst, D, y, s);
+    case 64: return launch_grouped_n<64>(d, x, B, C, dA_cs, dt_T, hst, D, y, part, s);
+    case 128: return launch_grouped_n<128>(d, x, B, C, dA_cs, dt_T, hst, D, y, part, s);
+    case 256: return launch_grouped_n<256>(d, x, B, C, dA_cs, dt_T, hst, D, y, part, s);
     default: return hipErrorInvalidValue;
   }
 }

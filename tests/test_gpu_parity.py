@@ -281,7 +281,8 @@ def test_bad_workspace_is_rejected_without_launch(m2):
 
 # The fused forward's grouped output stage serves several heads per workgroup;
 # these shapes give several head slices per group, a short last slice, G > 1,
-# every state size it supports, and a ragged last chunk.
+# every state size it supports (512 in two column-half passes), every chunk
+# size, and a ragged last chunk.
 GROUPED = [
     _custom(name="grp_N64_slices", batch=1, seqlen=16384 - 100, nheads=10, headdim=64, dstate=64,
             ngroups=2, chunk_size=256, init_state=True, seed=41),
@@ -291,6 +292,13 @@ GROUPED = [
             ngroups=4, chunk_size=64, init_state=True, seed=43),
     _custom(name="grp_N256_q128", batch=1, seqlen=6000, nheads=12, headdim=64, dstate=256,
             ngroups=3, chunk_size=128, seed=44),
+    # state size 512: two passes over column halves, float32 y in between
+    _custom(name="grp_N512_slices", batch=1, seqlen=8192 - 37, nheads=16, headdim=64,
+            dstate=512, ngroups=2, chunk_size=256, init_state=True, seed=45),
+    _custom(name="grp_N512_q64", batch=2, seqlen=2048 + 5, nheads=8, headdim=64, dstate=512,
+            ngroups=4, chunk_size=64, seed=46),
+    _custom(name="grp_N512_q128", batch=1, seqlen=3000, nheads=6, headdim=64, dstate=512,
+            ngroups=1, chunk_size=128, init_state=True, seed=47),
 ]
 
 
