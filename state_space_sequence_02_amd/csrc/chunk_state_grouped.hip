@@ -20,6 +20,11 @@
 // state term y_i += 2^cs[i] (h C_i) of the forward pass; only the row weights
 // differ (rows past the sequence end weigh 0).
 //
+// State size 512 runs as two launches over halves of the state columns (each
+// column of S depends only on the same column of B): each launch holds 256
+// columns of B^T operands, the register budget of state size 256, and
+// writes its half of every row of the [.., P, 512] states.
+//
 // Layout: N/32 waves; wave w owns the 32 state columns n0 = 32 w .. 32 w + 31
 // as NTW = 2 MFMA tiles, MFMA row m of tile nt standing for
 // n = n0 + 4 NTW (m/4) + 4 nt + m%4, so each lane stores 4 NTW consecutive n
@@ -78,7 +83,9 @@ template <int P, int Q, int N, bool ADJ>
 __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chunk_state_grouped_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ dA_cs,
     const float* __restrict__ dt_T, float* __restrict__ states, int L, int H, int G, int nc,
-    int hpw, int slices) {
+    int hpw, int slices, int ldn, int ncol0) {
+  // rows of B and of the states hold ldn columns; this launch covers
+  // columns ncol0 .. ncol0 + N - 1
   using K = SCfg<P, Q, N>;
   constexpr int NTW = K::NTW, PT = K::PT, KS = K::KS, BROW = K::BROW;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -115,7 +122,7 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
       const int64_t t = tok0 + jb * 64 + r;
       bf16x8 v;
       if (t < L) {
-        v = *(const bf16x8*)(Bm + (((int64_t)b * L + t) * G + g) * N + c8);
+        v = *(const bf16x8*)(Bm + (((int64_t)b * L + t) * G + g) * ldn + ncol0 + c8);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = f2bf(0.f);
@@ -194,10 +201,10 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
     }
     __builtin_amdgcn_s_waitcnt(0);  // next head's x landed; older stores drained
     // acc[nt][pt][r] = S[p = 16 pt + L16][n = n0 + 4 NTW grp + 4 nt + r]
-    float* out = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+    float* out = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * ldn + ncol0;
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
-      float* row = out + (int64_t)(16 * pt + L16) * N + n0 + 4 * NTW * grp;
+      float* row = out + (int64_t)(16 * pt + L16) * ldn + n0 + 4 * NTW * grp;
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) *(f32x4*)(row + 4 * nt) = acc[nt][pt];
     }
@@ -218,7 +225,7 @@ int cu_count_state() {
 
 template <int P, int Q, int N, bool ADJ>
 hipError_t launch_grouped(const Dims& d, const void* x, const void* B, const float* dA_cs,
-                          const float* dt_T, float* states, hipStream_t s) {
+                          const float* dt_T, float* states, int ncol0, hipStream_t s) {
   using K = SCfg<P, Q, N>;
   auto kern = chunk_state_grouped_kernel<P, Q, N, ADJ>;
   static const hipError_t attr = hipFuncSetAttribute(
@@ -235,7 +242,7 @@ hipError_t launch_grouped(const Dims& d, const void* x, const void* B, const flo
   const int64_t grid = d.B * d.nc * d.G * slices;
   kern<<<(unsigned)grid, K::NT, K::LDS, s>>>((const bf16*)x, (const bf16*)B, dA_cs, dt_T, states,
                                            (int)d.L, (int)d.H, (int)d.G, (int)d.nc, (int)hpw,
-                                           (int)slices);
+                                           (int)slices, (int)d.N, ncol0);
   return hipGetLastError();
 }
 
@@ -243,9 +250,14 @@ template <int Q, bool ADJ>
 hipError_t launch_grouped_n(const Dims& d, const void* x, const void* B, const float* dA_cs,
                             const float* dt_T, float* states, hipStream_t s) {
   switch (d.N) {
-    case 64: return launch_grouped<64, Q, 64, ADJ>(d, x, B, dA_cs, dt_T, states, s);
-    case 128: return launch_grouped<64, Q, 128, ADJ>(d, x, B, dA_cs, dt_T, states, s);
-    case 256: return launch_grouped<64, Q, 256, ADJ>(d, x, B, dA_cs, dt_T, states, s);
+    case 64: return launch_grouped<64, Q, 64, ADJ>(d, x, B, dA_cs, dt_T, states, 0, s);
+    case 128: return launch_grouped<64, Q, 128, ADJ>(d, x, B, dA_cs, dt_T, states, 0, s);
+    case 256: return launch_grouped<64, Q, 256, ADJ>(d, x, B, dA_cs, dt_T, states, 0, s);
+    case 512: {
+      const hipError_t e = launch_grouped<64, Q, 256, ADJ>(d, x, B, dA_cs, dt_T, states, 0, s);
+      if (e != hipSuccess) return e;
+      return launch_grouped<64, Q, 256, ADJ>(d, x, B, dA_cs, dt_T, states, 256, s);
+    }
     default: return hipErrorInvalidValue;
   }
 }
@@ -264,7 +276,7 @@ hipError_t launch_grouped_q(const Dims& d, const void* x, const void* B, const f
 }  // namespace
 
 bool grouped_state_supported(const Dims& d) {
-  return d.bf16 && d.P == 64 && (d.N == 64 || d.N == 128 || d.N == 256) &&
+  return d.bf16 && d.P == 64 && (d.N == 64 || d.N == 128 || d.N == 256 || d.N == 512) &&
          (d.Q == 64 || d.Q == 128 || d.Q == 256);
 }
 
