@@ -42,7 +42,7 @@ def span_plan(w, cus=256):
     None where the library runs chunk_state + state_passing (same rule as
     the library's dispatch: spans of 8, else 4, chunks while the grid gives
     every CU a workgroup; R = 4, 2 or 1 heads of a group likewise)."""
-    if not grouped_path(w) or w.dstate == 512:
+    if not grouped_path(w):
         return None
     nc = w.nchunks
     for K in (8, 4):

@@ -121,12 +121,12 @@ __device__ __forceinline__ void wait_vm(int n) {
 // c) into buffer `buf` (an LDS byte address): load k of the block goes to
 // wave k % NW.  Rows past L are clamped to L - 1: their weight is 0 (dt is
 // zero-padded).
-template <int Q, int N, int R>
+template <int Q, int N, int R, int LDN>
 __device__ __forceinline__ void issue_block(uint32_t buf, const bf16* __restrict__ x,
                                             const bf16* __restrict__ Bm,
                                             const float* __restrict__ dA_cs,
                                             const float* __restrict__ dt_T, int c, int jb, int b,
-                                            int h0, int g, int L, int H, int G, int nc) {
+                                            int h0, int g, int L, int H, int G, int nc, int ncol0) {
   using C = SpanCfg<Q, N, R>;
   const int lane = lane_id();
   const int w = wave_id();
@@ -146,7 +146,7 @@ __device__ __forceinline__ void issue_block(uint32_t buf, const bf16* __restrict
       const int row = s / (N / 8), pos = s % (N / 8);
       int64_t t = tok0 + row;
       if (t > L - 1) t = L - 1;
-      dma16(Bm + (((int64_t)b * L + t) * G + g) * N + 8 * sb<N>(row, pos),
+      dma16(Bm + (((int64_t)b * L + t) * G + g) * LDN + ncol0 + 8 * sb<N>(row, pos),
             buf + C::XS + s * 16);
     } else if (k == C::XT + C::BT) {  // cumulative sums and dt of the R heads
       const int r = lane >> 4, q = lane & 15;
@@ -166,7 +166,7 @@ __device__ __forceinline__ void issue_block(uint32_t buf, const bf16* __restrict
 // (dst[j]); block i's address is p[j] plus i times the slot's per-block
 // stride (per chunk for the last cumulative sums).  Valid while the block
 // lies inside the sequence (no clamping needed).
-template <int Q, int N, int R>
+template <int Q, int N, int R, int LDN>
 struct DmaPlan {
   using C = SpanCfg<Q, N, R>;
   static constexpr int NJ = (C::TOT + C::NW - 1) / C::NW;
@@ -177,7 +177,7 @@ struct DmaPlan {
   __device__ __forceinline__ void init(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
                                        const float* __restrict__ dA_cs,
                                        const float* __restrict__ dt_T, int c0, int b, int h0,
-                                       int g, int L, int H, int G, int nc) {
+                                       int g, int L, int H, int G, int nc, int ncol0) {
     const int lane = lane_id();
     const int w = wave_id();
     const int64_t tok0 = (int64_t)c0 * Q;
@@ -196,7 +196,8 @@ struct DmaPlan {
       } else if (k < C::XT + C::BT) {
         const int s = (k - C::XT) * 64 + lane;
         const int row = s / (N / 8), pos = s % (N / 8);
-        p[j] = (const char*)(Bm + (((int64_t)b * L + tok0 + row) * G + g) * N + 8 * sb<N>(row, pos));
+        p[j] = (const char*)(Bm + (((int64_t)b * L + tok0 + row) * G + g) * LDN + ncol0 +
+                             8 * sb<N>(row, pos));
         dst[j] = C::XS + (k - C::XT) * 1024;
         kind[j] = 1;
       } else if (k == C::XT + C::BT) {
@@ -218,7 +219,7 @@ struct DmaPlan {
   __device__ __forceinline__ void issue(uint32_t buf, int i, int H, int G) const {
     const int lane = lane_id();
     const int64_t xs = (int64_t)i * C::RB * H * C::P * 2;
-    const int64_t bstr = (int64_t)i * C::RB * G * N * 2;
+    const int64_t bstr = (int64_t)i * C::RB * G * LDN * 2;
     const int64_t cstr = (int64_t)i * C::RB * 4;
     const int64_t lstr = (int64_t)(i / C::BPC) * Q * 4;
 #pragma unroll
@@ -245,16 +246,16 @@ __device__ __forceinline__ int tile_cols(int w, int m) {  // 32-column group
   return NW >= R ? (w % (NW / R)) * R + m : m % NW;
 }
 
-template <int Q, int N, int R>
+template <int Q, int N, int R, int LDN>
 __device__ __forceinline__ void store_hst(bf16* __restrict__ hst, const f32x4 (&acc)[R][2][4],
                                           int b, int c, int h0, int H, int nc, int L16,
-                                          int grp, int w) {
+                                          int grp, int w, int ncol0) {
   using C = SpanCfg<Q, N, R>;
 #pragma unroll
   for (int m = 0; m < R; ++m) {
     const int r = tile_head<C::NW, R>(w, m);
     const int ncol = 32 * tile_cols<C::NW, R>(w, m) + 8 * grp;
-    bf16* dst = hst + ((((int64_t)b * nc + c) * H + h0 + r) * 64 + L16) * N + ncol;
+    bf16* dst = hst + ((((int64_t)b * nc + c) * H + h0 + r) * 64 + L16) * LDN + ncol0 + ncol;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       bf16x8 o;
@@ -263,17 +264,19 @@ __device__ __forceinline__ void store_hst(bf16* __restrict__ hst, const f32x4 (&
         o[e] = f2bf(acc[m][0][pt][e]);
         o[4 + e] = f2bf(acc[m][1][pt][e]);
       }
-      *(bf16x8*)(dst + (int64_t)16 * pt * N) = o;
+      *(bf16x8*)(dst + (int64_t)16 * pt * LDN) = o;
     }
   }
 }
 
-template <int Q, int N, int R, bool REPLAY>
+template <int Q, int N, int R, bool REPLAY, int LDN>
 __global__ void __launch_bounds__((SpanCfg<Q, N, R>::NT), (SpanCfg<Q, N, R>::WPE)) chunk_state_span_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ dA_cs,
     const float* __restrict__ dt_T, float* __restrict__ span_states,
     float* __restrict__ span_decay, bf16* __restrict__ hst, int L, int H, int G, int nc, int K,
-    int ng, int BNGG) {
+    int ng, int BNGG, int ncol0) {
+  // Rows of B, of the span states and of the chunk-start states hold LDN
+  // columns; this launch covers columns ncol0 .. ncol0 + N - 1.
   using C = SpanCfg<Q, N, R>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
@@ -305,12 +308,12 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R>::NT), (SpanCfg<Q, N, R>::WPE
   for (int m = 0; m < R; ++m) {
     const int r = tile_head<C::NW, R>(w, m);
     const int ncol = 32 * tile_cols<C::NW, R>(w, m) + 8 * grp;
-    const float* sst = span_states + (((int64_t)b * ng + s) * H + h0 + r) * 64 * N;
+    const float* sst = span_states + (((int64_t)b * ng + s) * H + h0 + r) * 64 * LDN + ncol0;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        acc[m][nt][pt] = REPLAY ? *(const f32x4*)(sst + (16 * pt + L16) * N + ncol + 4 * nt)
+        acc[m][nt][pt] = REPLAY ? *(const f32x4*)(sst + (16 * pt + L16) * LDN + ncol + 4 * nt)
                                 : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float dsum[R];
@@ -319,8 +322,8 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R>::NT), (SpanCfg<Q, N, R>::WPE
 
   const uint32_t sbase = lds_addr(smem);
   __builtin_amdgcn_s_waitcnt(0);  // the start states are in registers
-  DmaPlan<Q, N, R> plan;
-  plan.init(x, Bm, dA_cs, dt_T, c0, b, h0, g, L, H, G, nc);
+  DmaPlan<Q, N, R, LDN> plan;
+  plan.init(x, Bm, dA_cs, dt_T, c0, b, h0, g, L, H, G, nc, ncol0);
   // blocks from `nfast` on reach past the sequence end: their rows are clamped
   const int nfast = min(nblk, (int)(((int64_t)L - (int64_t)c0 * Q) / C::RB));
 #pragma unroll
@@ -328,8 +331,8 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R>::NT), (SpanCfg<Q, N, R>::WPE
     if (j < nfast)
       plan.issue(sbase + j * C::BUF, j, H, G);
     else if (j < nblk)
-      issue_block<Q, N, R>(sbase + j * C::BUF, x, Bm, dA_cs, dt_T, c0 + j / C::BPC,
-                           j % C::BPC, b, h0, g, L, H, G, nc);
+      issue_block<Q, N, R, LDN>(sbase + j * C::BUF, x, Bm, dA_cs, dt_T, c0 + j / C::BPC,
+                                j % C::BPC, b, h0, g, L, H, G, nc, ncol0);
   }
 
   for (int i = 0; i < nblk; ++i) {
@@ -351,8 +354,8 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R>::NT), (SpanCfg<Q, N, R>::WPE
       if (j < nfast)
         plan.issue(sbase + (j % C::NBUF) * C::BUF, j, H, G);
       else
-        issue_block<Q, N, R>(sbase + (j % C::NBUF) * C::BUF, x, Bm, dA_cs, dt_T,
-                             c0 + j / C::BPC, j % C::BPC, b, h0, g, L, H, G, nc);
+        issue_block<Q, N, R, LDN>(sbase + (j % C::NBUF) * C::BUF, x, Bm, dA_cs, dt_T,
+                                  c0 + j / C::BPC, j % C::BPC, b, h0, g, L, H, G, nc, ncol0);
     }
     unsigned char* cur = smem + (i % C::NBUF) * C::BUF;
     const float* csb = (const float*)(cur + C::XS + C::BS);
@@ -360,7 +363,7 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R>::NT), (SpanCfg<Q, N, R>::WPE
     if (jb == 0) {
 #pragma unroll
       for (int r = 0; r < R; ++r) dsum[r] += cl[4 * r + 3];
-      if (REPLAY) store_hst<Q, N, R>(hst, acc, b, c, h0, H, nc, L16, grp, w);
+      if (REPLAY) store_hst<Q, N, R, LDN>(hst, acc, b, c, h0, H, nc, L16, grp, w, ncol0);
 #pragma unroll
       for (int m = 0; m < R; ++m) {
         const float dec = fast_exp2(cl[4 * tile_head<C::NW, R>(w, m) + 3]);
@@ -421,22 +424,22 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R>::NT), (SpanCfg<Q, N, R>::WPE
   }
 
   if (REPLAY) {  // start state of the span's last chunk
-    store_hst<Q, N, R>(hst, acc, b, c1 - 1, h0, H, nc, L16, grp, w);
+    store_hst<Q, N, R, LDN>(hst, acc, b, c1 - 1, h0, H, nc, L16, grp, w, ncol0);
   } else {
 #pragma unroll
     for (int m = 0; m < R; ++m) {
       const int r = tile_head<C::NW, R>(w, m);
       const int ncol = 32 * tile_cols<C::NW, R>(w, m) + 8 * grp;
-      float* sst = span_states + (((int64_t)b * ng + s) * H + h0 + r) * 64 * N;
+      float* sst = span_states + (((int64_t)b * ng + s) * H + h0 + r) * 64 * LDN + ncol0;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          *(f32x4*)(sst + (16 * pt + L16) * N + ncol + 4 * nt) = acc[m][nt][pt];
+          *(f32x4*)(sst + (16 * pt + L16) * LDN + ncol + 4 * nt) = acc[m][nt][pt];
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (tid == 0) span_decay[((int64_t)b * H + h0 + r) * ng + s] = dsum[r];
+      if (tid == 0 && ncol0 == 0) span_decay[((int64_t)b * H + h0 + r) * ng + s] = dsum[r];
   }
 }
 
@@ -499,12 +502,12 @@ int span_heads(const Dims& d, int K) {
   return 1;
 }
 
-template <int Q, int N, int R, bool REPLAY>
+template <int Q, int N, int R, bool REPLAY, int LDN>
 hipError_t launch_span(const Dims& d, int K, const void* x, const void* B, const float* dA_cs,
                        const float* dt_T, float* span_states, float* span_decay, void* hst,
-                       hipStream_t s) {
+                       int ncol0, hipStream_t s) {
   using C = SpanCfg<Q, N, R>;
-  auto kern = chunk_state_span_kernel<Q, N, R, REPLAY>;
+  auto kern = chunk_state_span_kernel<Q, N, R, REPLAY, LDN>;
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
   if (attr != hipSuccess) return attr;
@@ -513,7 +516,8 @@ hipError_t launch_span(const Dims& d, int K, const void* x, const void* B, const
   const int64_t grid = (BNGG + 7) / 8 * 8 * (d.H / d.G / R);
   kern<<<(unsigned)grid, C::NT, C::LDS, s>>>((const bf16*)x, (const bf16*)B, dA_cs, dt_T,
                                            span_states, span_decay, (bf16*)hst, (int)d.L,
-                                           (int)d.H, (int)d.G, (int)d.nc, K, (int)ng, (int)BNGG);
+                                           (int)d.H, (int)d.G, (int)d.nc, K, (int)ng, (int)BNGG,
+                                           ncol0);
   return hipGetLastError();
 }
 
@@ -523,12 +527,25 @@ hipError_t launch_span_qn(const Dims& d, int K, const void* x, const void* B, co
                           hipStream_t s) {
 #define M2_SPAN(QQ, NN)                                                                    \
   if (d.Q == QQ && d.N == NN)                                                              \
-    return launch_span<QQ, NN, R, REPLAY>(d, K, x, B, dA_cs, dt_T, span_states, span_decay, \
-                                          hst, s);
+    return launch_span<QQ, NN, R, REPLAY, NN>(d, K, x, B, dA_cs, dt_T, span_states,         \
+                                              span_decay, hst, 0, s);
   M2_SPAN(64, 64) M2_SPAN(64, 128) M2_SPAN(64, 256)
   M2_SPAN(128, 64) M2_SPAN(128, 128) M2_SPAN(128, 256)
   M2_SPAN(256, 64) M2_SPAN(256, 128) M2_SPAN(256, 256)
 #undef M2_SPAN
+  // state size 512: two launches over halves of the state columns (each
+  // column of the state evolves on its own)
+#define M2_SPAN512(QQ)                                                                       \
+  if (d.Q == QQ && d.N == 512) {                                                             \
+    const hipError_t e = launch_span<QQ, 256, R, REPLAY, 512>(d, K, x, B, dA_cs, dt_T,       \
+                                                              span_states, span_decay, hst, \
+                                                              0, s);                         \
+    if (e != hipSuccess) return e;                                                           \
+    return launch_span<QQ, 256, R, REPLAY, 512>(d, K, x, B, dA_cs, dt_T, span_states,        \
+                                                span_decay, hst, 256, s);                    \
+  }
+  M2_SPAN512(64) M2_SPAN512(128) M2_SPAN512(256)
+#undef M2_SPAN512
   return hipErrorInvalidValue;
 }
 
@@ -547,7 +564,7 @@ hipError_t launch_span_r(const Dims& d, int K, int R, const void* x, const void*
 }  // namespace
 
 int span_chunks(const Dims& d) {
-  if (!(d.bf16 && d.P == 64 && (d.N == 64 || d.N == 128 || d.N == 256) &&
+  if (!(d.bf16 && d.P == 64 && (d.N == 64 || d.N == 128 || d.N == 256 || d.N == 512) &&
         (d.Q == 64 || d.Q == 128 || d.Q == 256)))
     return 0;
   // Spans of 8 chunks (else 4) when that still gives every CU a workgroup;

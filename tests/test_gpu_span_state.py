@@ -49,17 +49,21 @@ SHAPES = [
     _w("span_Q256_N64_G4_R2", 8192, 32, 64, 4, 256, Bn=4, seed=101),
     # N = 64 with 4 heads per workgroup: two heads per wave
     _w("span_Q64_N64_R4_ragged", 2000, 64, 64, 1, 64, Bn=4, seed=102),
+    # N = 512: two launches over halves of the state columns
+    _w("span_Q64_N512_G4_R4_ragged", 4096 - 19, 32, 512, 4, 64, Bn=4, seed=103),
+    _w("span_Q256_N512_G3_K4", 3000, 96, 512, 3, 256, init=False, seed=104),
 ]
 
 # (span length, heads per workgroup) each shape reaches on a 256-CU device
 EXPECT = {"span_Q64_N256_K8_last_span_one_chunk": (8, 1), "span_Q64_N256_R4_ragged": (8, 4),
           "span_Q128_N128_G2_R4": (8, 4), "span_Q256_N64_G4_R2": (8, 2),
-          "span_Q64_N64_R4_ragged": (8, 4)}
+          "span_Q64_N64_R4_ragged": (8, 4), "span_Q64_N512_G4_R4_ragged": (8, 4),
+          "span_Q256_N512_G3_K4": (4, 1)}
 
 
 def span_chunks(w, cus):
     """The span length the library picks for these sizes (0: no span path)."""
-    if not (w.dtype == "bf16" and w.headdim == 64 and w.dstate in (64, 128, 256)
+    if not (w.dtype == "bf16" and w.headdim == 64 and w.dstate in (64, 128, 256, 512)
             and w.chunk_size in (64, 128, 256)):
         return 0
     nc = -(-w.seqlen // w.chunk_size)
