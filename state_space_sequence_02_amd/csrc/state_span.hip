@@ -55,7 +55,7 @@ namespace {
 constexpr int kSpanHeads = M2_SPAN_HEADS;
 constexpr int kSpanOcc = M2_SPAN_OCC;
 
-template <int Q, int N, int R>
+template <int Q, int N, int R, int OCCT = kSpanOcc>
 struct SpanCfg {
   static constexpr int P = 64, RB = 32, NW = N / 32, NT = 64 * NW, PT = P / 16;
   static constexpr int XH = RB * P * 2;      // one head's x rows of a block (4 KB)
@@ -65,7 +65,7 @@ struct SpanCfg {
   static constexpr int CL = 256;             // per head: cs[Q-4 .. Q-1] of the block's chunk
   static constexpr int BUF = XS + BS + CS + CL;
   // workgroups per CU: the target, if two buffers each still fit
-  static constexpr int OCC = (160 * 1024 / (2 * BUF)) < kSpanOcc ? (160 * 1024 / (2 * BUF)) : kSpanOcc;
+  static constexpr int OCC = (160 * 1024 / (2 * BUF)) < OCCT ? (160 * 1024 / (2 * BUF)) : OCCT;
   static constexpr int WPE = (OCC * NW + 3) / 4;  // waves per SIMD to fit
   static constexpr int BPC = Q / RB;         // blocks per chunk
   static constexpr int XT = XS / 1024, BT = BS / 1024;
@@ -269,15 +269,15 @@ __device__ __forceinline__ void store_hst(bf16* __restrict__ hst, const f32x4 (&
   }
 }
 
-template <int Q, int N, int R, bool REPLAY, int LDN>
-__global__ void __launch_bounds__((SpanCfg<Q, N, R>::NT), (SpanCfg<Q, N, R>::WPE)) chunk_state_span_kernel(
+template <int Q, int N, int R, bool REPLAY, int LDN, int OCCT>
+__global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R, OCCT>::WPE)) chunk_state_span_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ dA_cs,
     const float* __restrict__ dt_T, float* __restrict__ span_states,
     float* __restrict__ span_decay, bf16* __restrict__ hst, int L, int H, int G, int nc, int K,
     int ng, int BNGG, int ncol0) {
   // Rows of B, of the span states and of the chunk-start states hold LDN
   // columns; this launch covers columns ncol0 .. ncol0 + N - 1.
-  using C = SpanCfg<Q, N, R>;
+  using C = SpanCfg<Q, N, R, OCCT>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   // Every run of a (batch, span, group) on one XCD: id = 8 r + xcd,
@@ -502,12 +502,12 @@ int span_heads(const Dims& d, int K) {
   return 1;
 }
 
-template <int Q, int N, int R, bool REPLAY, int LDN>
-hipError_t launch_span(const Dims& d, int K, const void* x, const void* B, const float* dA_cs,
-                       const float* dt_T, float* span_states, float* span_decay, void* hst,
-                       int ncol0, hipStream_t s) {
-  using C = SpanCfg<Q, N, R>;
-  auto kern = chunk_state_span_kernel<Q, N, R, REPLAY, LDN>;
+template <int Q, int N, int R, bool REPLAY, int LDN, int OCCT>
+hipError_t launch_span_occ(const Dims& d, int K, const void* x, const void* B,
+                           const float* dA_cs, const float* dt_T, float* span_states,
+                           float* span_decay, void* hst, int ncol0, hipStream_t s) {
+  using C = SpanCfg<Q, N, R, OCCT>;
+  auto kern = chunk_state_span_kernel<Q, N, R, REPLAY, LDN, OCCT>;
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
   if (attr != hipSuccess) return attr;
@@ -519,6 +519,25 @@ hipError_t launch_span(const Dims& d, int K, const void* x, const void* B, const
                                            (int)d.H, (int)d.G, (int)d.nc, K, (int)ng, (int)BNGG,
                                            ncol0);
   return hipGetLastError();
+}
+
+// One head per workgroup (the smallest grids): when the grid is larger than
+// the device, a ring sized for two workgroups per CU lets all of them run at
+// once (that kernel needs about 112 VGPRs, so two 8-wave workgroups fit);
+// otherwise the ring takes the whole LDS.
+template <int Q, int N, int R, bool REPLAY, int LDN>
+hipError_t launch_span(const Dims& d, int K, const void* x, const void* B, const float* dA_cs,
+                       const float* dt_T, float* span_states, float* span_decay, void* hst,
+                       int ncol0, hipStream_t s) {
+  if constexpr (R == 1 && kSpanOcc == 1) {
+    const int64_t ng = (d.nc + K - 1) / K;
+    const int64_t grid = (d.B * ng * d.G + 7) / 8 * 8 * d.H / d.G;
+    if (grid > cu_count_span())
+      return launch_span_occ<Q, N, R, REPLAY, LDN, 2>(d, K, x, B, dA_cs, dt_T, span_states,
+                                                      span_decay, hst, ncol0, s);
+  }
+  return launch_span_occ<Q, N, R, REPLAY, LDN, kSpanOcc>(d, K, x, B, dA_cs, dt_T, span_states,
+                                                         span_decay, hst, ncol0, s);
 }
 
 template <int R, bool REPLAY>
