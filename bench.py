@@ -41,15 +41,18 @@ def span_plan(w, cus=256):
     """(span length K, heads per workgroup R) of the forward's span path, or
     None where the library runs chunk_state + state_passing (same rule as
     the library's dispatch: spans of 8, else 4, chunks while the grid gives
-    every CU a workgroup; R = 4, 2 or 1 heads of a group likewise)."""
+    every CU a workgroup; R = 4, 2 or 1 heads of a group likewise, at most 2
+    at N = 128 and 1 at N = 64)."""
     if not grouped_path(w):
         return None
     nc = w.nchunks
+    max_r = 1 if w.dstate == 64 else 2 if w.dstate == 128 else 4
     for K in (8, 4):
         ng = -(-nc // K)
         if nc >= K and w.batch * w.nheads * ng >= cus:
             for R in (4, 2):
-                if (w.nheads // w.ngroups) % R == 0 and w.batch * ng * w.nheads // R >= cus:
+                if (R <= max_r and (w.nheads // w.ngroups) % R == 0
+                        and w.batch * ng * w.nheads // R >= cus):
                     return K, R
             return K, 1
     return None
@@ -452,6 +455,12 @@ def sweep_bench(args):
             ms = e0.elapsed_time(e1) / n
             model = stage_model(w, cus)
             names = forward_stages(w, cus)
+            st_ms = [0.0] * 4
+            for _ in range(10):
+                ms4 = m2.mamba2_ssd_forward_profile(dims, g["x"], g["dt"], g["A"], g["B"], g["C"],
+                                                    g["D"], g["init_state"], y, fin, ws, need,
+                                                    stream)
+                st_ms = [a + b / 10 for a, b in zip(st_ms, ms4)]
             byt = sum(model[s]["bytes"] for s in names)
             flo = sum(model[s]["flops"] for s in names)
             plan = span_plan(w, cus)
@@ -465,7 +474,8 @@ def sweep_bench(args):
                 "algorithmic_bytes": byt, "GB/s": round(byt / (ms * 1e-3) / 1e9, 1),
                 "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
                 "TFLOP/s": round(flo / (ms * 1e-3) / 1e12, 1),
-                "mfma_frac": round(flo / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 3)}),
+                "mfma_frac": round(flo / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 3),
+                "stage_ms": {s: round(t, 4) for s, t in zip(names, st_ms)}}),
                 flush=True)
             del g, y, fin, ws
             torch.cuda.empty_cache()

@@ -493,11 +493,14 @@ int cu_count_span() {
   return n;
 }
 
-// Heads per workgroup: as many as share B (4, 2 or 1, a divisor of the
-// group's heads) while the grid still gives every CU a workgroup.
+// Heads per workgroup: as many as share B (a divisor of the group's heads)
+// while the grid still gives every CU a workgroup: up to 4 at N >= 256, 2 at
+// N = 128 and 1 at N = 64, where a workgroup has only N/32 waves and several
+// workgroups must share a CU to keep about eight waves on it.
 int span_heads(const Dims& d, int K) {
   const int64_t HG = d.H / d.G, ng = (d.nc + K - 1) / K;
-  for (int R = kSpanHeads; R > 1; R /= 2)
+  const int maxR = d.N == 64 ? 1 : d.N == 128 ? 2 : kSpanHeads;
+  for (int R = maxR; R > 1; R /= 2)
     if (HG % R == 0 && d.B * ng * d.H / R >= cu_count_span()) return R;
   return 1;
 }
@@ -521,18 +524,25 @@ hipError_t launch_span_occ(const Dims& d, int K, const void* x, const void* B,
   return hipGetLastError();
 }
 
-// One head per workgroup (the smallest grids): when the grid is larger than
-// the device, a ring sized for two workgroups per CU lets all of them run at
-// once (that kernel needs about 112 VGPRs, so two 8-wave workgroups fit);
-// otherwise the ring takes the whole LDS.
+// Workgroups per CU the LDS ring is sized for.  One by default (the ring
+// takes the whole LDS); where the grid is larger than the device and the
+// kernel is small enough for several workgroups per CU (one head per
+// workgroup, about 112 VGPRs; or N <= 128, at most 4 waves per workgroup), a
+// ring sized for two, or four at N = 64, lets more of the grid run at once.
 template <int Q, int N, int R, bool REPLAY, int LDN>
 hipError_t launch_span(const Dims& d, int K, const void* x, const void* B, const float* dA_cs,
                        const float* dt_T, float* span_states, float* span_decay, void* hst,
                        int ncol0, hipStream_t s) {
-  if constexpr (R == 1 && kSpanOcc == 1) {
+  if constexpr (kSpanOcc == 1 && (R == 1 || (N == 128 && R == 2))) {
     const int64_t ng = (d.nc + K - 1) / K;
-    const int64_t grid = (d.B * ng * d.G + 7) / 8 * 8 * d.H / d.G;
-    if (grid > cu_count_span())
+    const int64_t grid = (d.B * ng * d.G + 7) / 8 * 8 * (d.H / d.G / R);
+    const int64_t cus = cu_count_span();
+    if constexpr (N == 64) {
+      if (grid > 2 * cus)
+        return launch_span_occ<Q, N, R, REPLAY, LDN, 4>(d, K, x, B, dA_cs, dt_T, span_states,
+                                                        span_decay, hst, ncol0, s);
+    }
+    if (grid > cus)
       return launch_span_occ<Q, N, R, REPLAY, LDN, 2>(d, K, x, B, dA_cs, dt_T, span_states,
                                                       span_decay, hst, ncol0, s);
   }

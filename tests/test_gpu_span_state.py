@@ -45,10 +45,10 @@ SHAPES = [
     _w("span_Q256_N256_K4", 4096, 64, 256, 1, 256, seed=98),
     # several heads per workgroup (sharing the B rows)
     _w("span_Q64_N256_R4_ragged", 8155, 64, 256, 1, 64, seed=99),
-    _w("span_Q128_N128_G2_R4", 8192, 64, 128, 2, 128, Bn=2, init=False, seed=100),
-    _w("span_Q256_N64_G4_R2", 8192, 32, 64, 4, 256, Bn=4, seed=101),
-    # N = 64 with 4 heads per workgroup: two heads per wave
-    _w("span_Q64_N64_R4_ragged", 2000, 64, 64, 1, 64, Bn=4, seed=102),
+    _w("span_Q128_N128_G2_R2", 8192, 64, 128, 2, 128, Bn=2, init=False, seed=100),
+    _w("span_Q256_N64_G4_R1", 8192, 32, 64, 4, 256, Bn=4, seed=101),
+    # N = 64, one head per workgroup, four workgroups per CU
+    _w("span_Q64_N64_R1_ragged", 2000, 64, 64, 1, 64, Bn=4, seed=102),
     # N = 512: two launches over halves of the state columns
     _w("span_Q64_N512_G4_R4_ragged", 4096 - 19, 32, 512, 4, 64, Bn=4, seed=103),
     _w("span_Q256_N512_G3_K4", 3000, 96, 512, 3, 256, init=False, seed=104),
@@ -56,8 +56,8 @@ SHAPES = [
 
 # (span length, heads per workgroup) each shape reaches on a 256-CU device
 EXPECT = {"span_Q64_N256_K8_last_span_one_chunk": (8, 1), "span_Q64_N256_R4_ragged": (8, 4),
-          "span_Q128_N128_G2_R4": (8, 4), "span_Q256_N64_G4_R2": (8, 2),
-          "span_Q64_N64_R4_ragged": (8, 4), "span_Q64_N512_G4_R4_ragged": (8, 4),
+          "span_Q128_N128_G2_R2": (8, 2), "span_Q256_N64_G4_R1": (8, 1),
+          "span_Q64_N64_R1_ragged": (8, 1), "span_Q64_N512_G4_R4_ragged": (8, 4),
           "span_Q256_N512_G3_K4": (4, 1)}
 
 
@@ -74,12 +74,15 @@ def span_chunks(w, cus):
 
 
 def span_heads(w, K, cus):
-    """Heads per workgroup the library picks: 4, 2 or 1, a divisor of the
-    group's heads, while the grid still gives every CU a workgroup."""
+    """Heads per workgroup the library picks: 4, 2 or 1 (at most 2 at N = 128
+    and 1 at N = 64), a divisor of the group's heads, while the grid still
+    gives every CU a workgroup."""
     nc = -(-w.seqlen // w.chunk_size)
     ng = -(-nc // K)
+    max_r = 1 if w.dstate == 64 else 2 if w.dstate == 128 else 4
     for R in (4, 2):
-        if (w.nheads // w.ngroups) % R == 0 and w.batch * ng * w.nheads // R >= cus:
+        if (R <= max_r and (w.nheads // w.ngroups) % R == 0
+                and w.batch * ng * w.nheads // R >= cus):
             return R
     return 1
 
