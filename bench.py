@@ -41,20 +41,21 @@ def span_plan(w, cus=256):
     """(span length K, heads per workgroup R) of the forward's span path, or
     None where the library runs chunk_state + state_passing (same rule as
     the library's dispatch: spans of 8, else 4, chunks while the grid gives
-    every CU a workgroup; R = 4, 2 or 1 heads of a group likewise, at most 2
+    every CU two (batch, span, head) units, else one; R = 4, 2 or 1 heads of a group likewise, at most 2
     at N = 128 and 1 at N = 64)."""
     if not grouped_path(w):
         return None
     nc = w.nchunks
     max_r = 1 if w.dstate == 64 else 2 if w.dstate == 128 else 4
-    for K in (8, 4):
-        ng = -(-nc // K)
-        if nc >= K and w.batch * w.nheads * ng >= cus:
-            for R in (4, 2):
-                if (R <= max_r and (w.nheads // w.ngroups) % R == 0
-                        and w.batch * ng * w.nheads // R >= cus):
-                    return K, R
-            return K, 1
+    for want in (2 * cus, cus):
+        for K in (8, 4):
+            ng = -(-nc // K)
+            if nc >= K and w.batch * w.nheads * ng >= want:
+                for R in (4, 2):
+                    if (R <= max_r and (w.nheads // w.ngroups) % R == 0
+                            and w.batch * ng * w.nheads // R >= cus):
+                        return K, R
+                return K, 1
     return None
 
 

@@ -596,13 +596,16 @@ int span_chunks(const Dims& d) {
   if (!(d.bf16 && d.P == 64 && (d.N == 64 || d.N == 128 || d.N == 256 || d.N == 512) &&
         (d.Q == 64 || d.Q == 128 || d.Q == 256)))
     return 0;
-  // Spans of 8 chunks (else 4) when that still gives every CU a workgroup;
+  // Spans of 8 chunks when that gives every CU two (batch, span, head)
+  // units, else spans of 4 if they do (each workgroup then walks half as many
+  // blocks in sequence), else the longest span that gives every CU one;
   // shorter spans save too little of the state traffic.
   const int64_t cus = cu_count_span();
-  for (int K = 8; K >= 4; K /= 2) {
-    const int64_t ng = (d.nc + K - 1) / K;
-    if (d.nc >= K && d.B * d.H * ng >= cus) return K;
-  }
+  for (int64_t want = 2 * cus; want >= cus; want -= cus)
+    for (int K = 8; K >= 4; K /= 2) {
+      const int64_t ng = (d.nc + K - 1) / K;
+      if (d.nc >= K && d.B * d.H * ng >= want) return K;
+    }
   return 0;
 }
 

@@ -36,7 +36,7 @@ def _w(name, L, H, N, G, Q, Bn=1, init=True, seed=0):
 
 SHAPES = [
     _w("span_Q64_N64_G2_K4", 1000, 64, 64, 2, 64, seed=91),
-    _w("span_Q64_N256_K8_last_span_one_chunk", 2085, 32, 256, 1, 64, Bn=2, seed=92),
+    _w("span_Q64_N256_last_span_one_chunk", 2085, 32, 256, 1, 64, Bn=2, seed=92),
     _w("span_Q128_N128_G3_K4", 5115, 48, 128, 3, 128, init=False, seed=93),
     _w("span_Q256_N64_G4_ragged", 3996, 64, 64, 4, 256, seed=94),
     _w("span_Q128_N256_B2_K4", 4097, 16, 256, 1, 128, Bn=2, seed=95),
@@ -55,21 +55,24 @@ SHAPES = [
 ]
 
 # (span length, heads per workgroup) each shape reaches on a 256-CU device
-EXPECT = {"span_Q64_N256_K8_last_span_one_chunk": (8, 1), "span_Q64_N256_R4_ragged": (8, 4),
+EXPECT = {"span_Q64_N256_last_span_one_chunk": (4, 2), "span_Q64_N256_R4_ragged": (8, 4),
           "span_Q128_N128_G2_R2": (8, 2), "span_Q256_N64_G4_R1": (8, 1),
           "span_Q64_N64_R1_ragged": (8, 1), "span_Q64_N512_G4_R4_ragged": (8, 4),
           "span_Q256_N512_G3_K4": (4, 1)}
 
 
 def span_chunks(w, cus):
-    """The span length the library picks for these sizes (0: no span path)."""
+    """The span length the library picks for these sizes (0: no span path):
+    8 chunks if that gives every CU two (batch, span, head) units, else 4 if
+    that does, else the longest span that gives every CU one."""
     if not (w.dtype == "bf16" and w.headdim == 64 and w.dstate in (64, 128, 256, 512)
             and w.chunk_size in (64, 128, 256)):
         return 0
     nc = -(-w.seqlen // w.chunk_size)
-    for K in (8, 4):
-        if nc >= K and w.batch * w.nheads * (-(-nc // K)) >= cus:
-            return K
+    for want in (2 * cus, cus):
+        for K in (8, 4):
+            if nc >= K and w.batch * w.nheads * (-(-nc // K)) >= want:
+                return K
     return 0
 
 
