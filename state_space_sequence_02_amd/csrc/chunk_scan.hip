@@ -281,6 +281,82 @@ hipError_t launch_bf16_q(const Dims& d, const void* x, const void* B, const void
   }
 }
 
+// The same float32 arithmetic, in the same order, with one workgroup per
+// (b, c, h) for sizes where the chunk fits in LDS: the chunk's C, B and x
+// rows, its start state, cumulative sums and dt are staged once, then the
+// decayed in-chunk weights W[i][j] = (C_i . B_j) 2^(cs_i - cs_j) dt_j (j <= i)
+// are formed once per chunk by the whole workgroup, and each output is the
+// carried-state dot product plus one pass over W's row.  The plain kernel
+// above reloads C, B and x rows from global memory inside its inner loops
+// and recomputes C_i . B_j for every output column.
+__global__ void __launch_bounds__(256) chunk_scan_f32_lds_kernel(
+    const float* __restrict__ x, const float* __restrict__ Bm, const float* __restrict__ Cm,
+    const float* __restrict__ dA_cs, const float* __restrict__ dt_T,
+    const float* __restrict__ states, const float* __restrict__ Dv, float* __restrict__ y, int L,
+    int H, int G, int P, int N, int Q, int nc) {
+  extern __shared__ float sm[];
+  float* Cs = sm;            // [Q][N]
+  float* Bs = Cs + Q * N;    // [Q][N]
+  float* Xs = Bs + Q * N;    // [Q][P]
+  float* Hs = Xs + Q * P;    // [P][N]
+  float* css = Hs + P * N;   // [Q]
+  float* dts = css + Q;      // [Q]
+  float* W = dts + Q;        // [Q][Q], lower triangle used
+  const int h = blockIdx.x % H;
+  const int c = (blockIdx.x / H) % nc;
+  const int b = blockIdx.x / (H * nc);
+  const int g = h / (H / G);
+  const int64_t tok0 = (int64_t)c * Q;
+  const int valid = (int)min((int64_t)Q, (int64_t)L - tok0);
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < valid * N; idx += blockDim.x) {
+    const int r = idx / N, n = idx % N;
+    const int64_t off = (((int64_t)b * L + tok0 + r) * G + g) * N + n;
+    Cs[idx] = Cm[off];
+    Bs[idx] = Bm[off];
+  }
+  for (int idx = tid; idx < valid * P; idx += blockDim.x) {
+    const int r = idx / P, p = idx % P;
+    Xs[idx] = x[(((int64_t)b * L + tok0 + r) * H + h) * P + p];
+  }
+  const float* hsrc = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+  for (int idx = tid; idx < P * N; idx += blockDim.x) Hs[idx] = hsrc[idx];
+  const int64_t cbase = (((int64_t)b * H + h) * nc + c) * Q;
+  for (int idx = tid; idx < valid; idx += blockDim.x) {
+    css[idx] = dA_cs[cbase + idx];
+    dts[idx] = dt_T[cbase + idx];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < valid * valid; idx += blockDim.x) {
+    const int i = idx / valid, j = idx % valid;
+    if (j > i) continue;
+    const float* Ci = Cs + i * N;
+    const float* Bj = Bs + j * N;
+    float cb = 0.f;
+    for (int n = 0; n < N; ++n) cb += Ci[n] * Bj[n];
+    W[i * Q + j] = cb * exp2f(css[i] - css[j]) * dts[j];
+  }
+  __syncthreads();
+  const float Dh = Dv ? Dv[h] : 0.f;
+  for (int o = tid; o < valid * P; o += blockDim.x) {
+    const int i = o / P, p = o % P;
+    const float* Ci = Cs + i * N;
+    const float* hp = Hs + p * N;
+    float inter = 0.f;
+    for (int n = 0; n < N; ++n) inter += Ci[n] * hp[n];
+    float acc = exp2f(css[i]) * inter;
+    for (int j = 0; j <= i; ++j) acc += W[i * Q + j] * Xs[j * P + p];
+    if (Dv) acc += Dh * Xs[i * P + p];
+    y[(((int64_t)b * L + tok0 + i) * H + h) * P + p] = acc;
+  }
+}
+
+// LDS bytes the staged float32 kernel needs, if it fits in 64 KB (else 0).
+size_t f32_lds_bytes(const Dims& d) {
+  const int64_t n = 2 * d.Q * d.N + d.Q * d.P + d.P * d.N + 2 * d.Q + d.Q * d.Q;
+  return n * 4 <= 64 * 1024 ? (size_t)n * 4 : 0;
+}
+
 }  // namespace
 
 hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* B, const void* C,
@@ -293,6 +369,15 @@ hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* B, const 
       case 128: return launch_bf16_q<128>(d, x, B, C, dA_cs, dt_T, states, D, y, s);
       default: return hipErrorInvalidValue;
     }
+  }
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)chunk_scan_f32_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+      64 * 1024);
+  if (const size_t lds = attr == hipSuccess ? f32_lds_bytes(d) : 0) {
+    chunk_scan_f32_lds_kernel<<<(unsigned)(d.B * d.nc * d.H), 256, lds, s>>>(
+        (const float*)x, (const float*)B, (const float*)C, dA_cs, dt_T, states, D, (float*)y,
+        (int)d.L, (int)d.H, (int)d.G, (int)d.P, (int)d.N, (int)d.Q, (int)d.nc);
+    return hipGetLastError();
   }
   const int64_t total = d.B * d.L * d.H * d.P;
   chunk_scan_f32_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(

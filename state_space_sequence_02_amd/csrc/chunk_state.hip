@@ -158,6 +158,52 @@ __global__ void __launch_bounds__(256) chunk_state_f32_kernel(
   states[gid] = acc;
 }
 
+// The same float32 arithmetic, in the same order, with one workgroup per
+// (b, c, h): the chunk's x and B rows and the row weights w_j are staged in
+// LDS once, where they fit, instead of being reloaded by every thread.
+__global__ void __launch_bounds__(256) chunk_state_f32_lds_kernel(
+    const float* __restrict__ x, const float* __restrict__ Bm, const float* __restrict__ dA_cs,
+    const float* __restrict__ dt_T, float* __restrict__ states, int L, int H, int G, int P,
+    int N, int Q, int nc) {
+  extern __shared__ float sm[];
+  float* Xs = sm;            // [Q][P]
+  float* Bs = Xs + Q * P;    // [Q][N]
+  float* ws = Bs + Q * N;    // [Q]
+  const int h = blockIdx.x % H;
+  const int c = (blockIdx.x / H) % nc;
+  const int b = blockIdx.x / (H * nc);
+  const int g = h / (H / G);
+  const int64_t tok0 = (int64_t)c * Q;
+  const int valid = (int)min((int64_t)Q, (int64_t)L - tok0);
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < valid * P; idx += blockDim.x) {
+    const int r = idx / P, p = idx % P;
+    Xs[idx] = x[(((int64_t)b * L + tok0 + r) * H + h) * P + p];
+  }
+  for (int idx = tid; idx < valid * N; idx += blockDim.x) {
+    const int r = idx / N, n = idx % N;
+    Bs[idx] = Bm[(((int64_t)b * L + tok0 + r) * G + g) * N + n];
+  }
+  const int64_t cbase = (((int64_t)b * H + h) * nc + c) * Q;
+  const float cs_last = dA_cs[cbase + Q - 1];
+  for (int j = tid; j < valid; j += blockDim.x)
+    ws[j] = exp2f(cs_last - dA_cs[cbase + j]) * dt_T[cbase + j];
+  __syncthreads();
+  float* out = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+  for (int o = tid; o < P * N; o += blockDim.x) {
+    const int p = o / N, n = o % N;
+    float acc = 0.f;
+    for (int j = 0; j < valid; ++j) acc += ws[j] * Xs[j * P + p] * Bs[j * N + n];
+    out[o] = acc;
+  }
+}
+
+// LDS bytes the staged float32 kernel needs, if it fits in 64 KB (else 0).
+size_t f32_state_lds_bytes(const Dims& d) {
+  const int64_t n = d.Q * d.P + d.Q * d.N + d.Q;
+  return n * 4 <= 64 * 1024 ? (size_t)n * 4 : 0;
+}
+
 template <int P, int NTW>
 hipError_t launch_bf16(const Dims& d, const void* x, const void* B, const float* dA_cs,
                        const float* dt_T, float* states, hipStream_t s) {
@@ -185,6 +231,15 @@ hipError_t launch_chunk_state(const Dims& d, const void* x, const void* B, const
       case 128: return launch_bf16<128, 2>(d, x, B, dA_cs, dt_T, states, s);
       default: return hipErrorInvalidValue;
     }
+  }
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)chunk_state_f32_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+      64 * 1024);
+  if (const size_t lds = attr == hipSuccess ? f32_state_lds_bytes(d) : 0) {
+    chunk_state_f32_lds_kernel<<<(unsigned)(d.B * d.nc * d.H), 256, lds, s>>>(
+        (const float*)x, (const float*)B, dA_cs, dt_T, states, (int)d.L, (int)d.H, (int)d.G,
+        (int)d.P, (int)d.N, (int)d.Q, (int)d.nc);
+    return hipGetLastError();
   }
   const int64_t total = d.B * d.nc * d.H * d.P * d.N;
   chunk_state_f32_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
