@@ -235,8 +235,10 @@ struct DmaPlan {
 
 // Which part of the run's states tile m of wave w holds: R tiles of 32 state
 // columns each (all 64 rows as 2 x 4 MFMA tiles).  With R <= NW the NW / R
-// waves of a head split its N columns, so a wave contracts one head's x rows;
-// with more heads than waves (N = 64), a wave holds R / NW heads whole.
+// waves of a head split its N columns, so a wave contracts one head's x rows.
+// More heads than waves (a wave holding R / NW heads whole) is supported for
+// every instantiation, though the host's head rule (at most 1 head per
+// workgroup at N = 64 and 2 at N = 128) no longer picks it.
 template <int NW, int R>
 __device__ __forceinline__ int tile_head(int w, int m) {
   return NW >= R ? w / (NW / R) : w * (R / NW) + m / NW;
