@@ -337,19 +337,55 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
                                 j % C::BPC, b, h0, g, L, H, G, nc, ncol0);
   }
 
+  // x rows of the block in buffer `bp` scaled by w_j in place: slot s is
+  // head s / 256, row (s % 256) / 8
+  auto scale_x = [&](unsigned char* bp) {
+    const float* sb_ = (const float*)(bp + C::XS + C::BS);
+    const float* cl_ = (const float*)(bp + C::XS + C::BS + C::CS);
+#pragma unroll
+    for (int s0 = 0; s0 < C::SLOTS; s0 += C::NT) {
+      const int sl = s0 + tid;
+      if (C::SLOTS % C::NT == 0 || sl < C::SLOTS) {
+        const int r = sl >> 8, row = (sl & 255) >> 3;
+        const bf16x8 v = *(const bf16x8*)(bp + sl * 16);
+        const float wr = fast_exp2(cl_[4 * r + 3] - sb_[64 * r + row]) * sb_[64 * r + 32 + row];
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = f2bf(bf2f(v[e]) * wr);
+        *(bf16x8*)(bp + sl * 16) = o;
+      }
+    }
+  };
+  // Software pipeline: block i + 1 is scaled while block i's MFMAs run (they
+  // touch different buffers), so each block needs one barrier.  Block 0 is
+  // scaled first.
+  static_assert(C::NBUF >= 3, "the block being scaled, the block being read and the one loading");
+  if (nblk > 0) {
+    asm volatile("" ::: "memory");
+    wait_vm(nw * min(C::NBUF - 2, nblk - 1));
+    __builtin_amdgcn_s_barrier();  // block 0 landed for every wave
+    asm volatile("" ::: "memory");
+    scale_x(smem);
+  }
+
   for (int i = 0; i < nblk; ++i) {
     const int c = c0 + i / C::BPC, jb = i % C::BPC;
-    // operations newer than block i's loads: the loads of the blocks after it
-    // already issued, and the start-state stores issued since
-    int newer = nw * (min(i + C::NBUF - 2, nblk - 1) - i);
-    if (REPLAY) {
-      const int j0 = max(0, i - C::NBUF + 1);
-      const int starts = (i - 1) / C::BPC - (j0 - 1 + C::BPC) / C::BPC + 1;  // j0 <= j <= i-1, j % BPC == 0
-      newer += 4 * R * (i > j0 ? max(starts, 0) : 0);
+    // operations newer than block i + 1's loads: the loads of the blocks after
+    // it already issued, and the start-state stores issued since (after the
+    // last block nothing is left to wait for but this wave's LDS writes)
+    int newer = 0;
+    if (i + 1 < nblk) {
+      newer = nw * (min(i + C::NBUF - 2, nblk - 1) - (i + 1));
+      if (REPLAY) {
+        const int j0 = max(0, i + 2 - C::NBUF);
+        const int starts = (i - 1) / C::BPC - (j0 - 1 + C::BPC) / C::BPC + 1;  // j0 <= j <= i-1, j % BPC == 0
+        newer += 4 * R * (i > j0 ? max(starts, 0) : 0);
+      }
     }
     asm volatile("" ::: "memory");
     wait_vm(newer);
-    __builtin_amdgcn_s_barrier();  // block i landed for every wave; block i - 1 fully read
+    // block i + 1 landed and block i scaled, for every wave; block i - 1 fully read
+    __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (i + C::NBUF - 1 < nblk) {
       const int j = i + C::NBUF - 1;
@@ -360,7 +396,6 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
                                   c0 + j / C::BPC, j % C::BPC, b, h0, g, L, H, G, nc, ncol0);
     }
     unsigned char* cur = smem + (i % C::NBUF) * C::BUF;
-    const float* csb = (const float*)(cur + C::XS + C::BS);
     const float* cl = (const float*)(cur + C::XS + C::BS + C::CS);
     if (jb == 0) {
 #pragma unroll
@@ -376,21 +411,7 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
         }
       }
     }
-    // scale the x rows by w_j in place: slot s is head s / 256, row (s % 256) / 8
-#pragma unroll
-    for (int s0 = 0; s0 < C::SLOTS; s0 += C::NT) {
-      const int sl = s0 + tid;
-      if (C::SLOTS % C::NT == 0 || sl < C::SLOTS) {
-        const int r = sl >> 8, row = (sl & 255) >> 3;
-        const bf16x8 v = *(const bf16x8*)(cur + sl * 16);
-        const float wr = fast_exp2(cl[4 * r + 3] - csb[64 * r + row]) * csb[64 * r + 32 + row];
-        bf16x8 o;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = f2bf(bf2f(v[e]) * wr);
-        *(bf16x8*)(cur + sl * 16) = o;
-      }
-    }
-    lds_barrier();
+    if (i + 1 < nblk) scale_x(smem + ((i + 1) % C::NBUF) * C::BUF);
     const unsigned char* bsm = cur + C::XS;
     const int ra = 8 * grp + (L16 >> 2), rb = ra + 4;
     constexpr int HPW = R > C::NW ? R / C::NW : 1;  // heads per wave
