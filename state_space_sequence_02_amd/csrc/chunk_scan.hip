@@ -295,9 +295,10 @@ __global__ void __launch_bounds__(256) chunk_scan_f32_lds_kernel(
     const float* __restrict__ states, const float* __restrict__ Dv, float* __restrict__ y, int L,
     int H, int G, int P, int N, int Q, int nc) {
   extern __shared__ float sm[];
-  float* Cs = sm;            // [Q][N]
-  float* Bs = Cs + Q * N;    // [Q][N]
-  float* Xs = Bs + Q * N;    // [Q][P]
+  const int NS = N + 1;      // C and B row stride: neighbouring rows in different banks
+  float* Cs = sm;            // [Q][NS]
+  float* Bs = Cs + Q * NS;   // [Q][NS]
+  float* Xs = Bs + Q * NS;   // [Q][P]
   float* Hs = Xs + Q * P;    // [P][N]
   float* css = Hs + P * N;   // [Q]
   float* dts = css + Q;      // [Q]
@@ -312,8 +313,8 @@ __global__ void __launch_bounds__(256) chunk_scan_f32_lds_kernel(
   for (int idx = tid; idx < valid * N; idx += blockDim.x) {
     const int r = idx / N, n = idx % N;
     const int64_t off = (((int64_t)b * L + tok0 + r) * G + g) * N + n;
-    Cs[idx] = Cm[off];
-    Bs[idx] = Bm[off];
+    Cs[r * NS + n] = Cm[off];
+    Bs[r * NS + n] = Bm[off];
   }
   for (int idx = tid; idx < valid * P; idx += blockDim.x) {
     const int r = idx / P, p = idx % P;
@@ -330,8 +331,8 @@ __global__ void __launch_bounds__(256) chunk_scan_f32_lds_kernel(
   for (int idx = tid; idx < valid * valid; idx += blockDim.x) {
     const int i = idx / valid, j = idx % valid;
     if (j > i) continue;
-    const float* Ci = Cs + i * N;
-    const float* Bj = Bs + j * N;
+    const float* Ci = Cs + i * NS;
+    const float* Bj = Bs + j * NS;
     float cb = 0.f;
     for (int n = 0; n < N; ++n) cb += Ci[n] * Bj[n];
     W[i * Q + j] = cb * exp2f(css[i] - css[j]) * dts[j];
@@ -340,7 +341,7 @@ __global__ void __launch_bounds__(256) chunk_scan_f32_lds_kernel(
   const float Dh = Dv ? Dv[h] : 0.f;
   for (int o = tid; o < valid * P; o += blockDim.x) {
     const int i = o / P, p = o % P;
-    const float* Ci = Cs + i * N;
+    const float* Ci = Cs + i * NS;
     const float* hp = Hs + p * N;
     float inter = 0.f;
     for (int n = 0; n < N; ++n) inter += Ci[n] * hp[n];
@@ -353,7 +354,7 @@ __global__ void __launch_bounds__(256) chunk_scan_f32_lds_kernel(
 
 // LDS bytes the staged float32 kernel needs, if it fits in 64 KB (else 0).
 size_t f32_lds_bytes(const Dims& d) {
-  const int64_t n = 2 * d.Q * d.N + d.Q * d.P + d.P * d.N + 2 * d.Q + d.Q * d.Q;
+  const int64_t n = 2 * d.Q * (d.N + 1) + d.Q * d.P + d.P * d.N + 2 * d.Q + d.Q * d.Q;
   return n * 4 <= 64 * 1024 ? (size_t)n * 4 : 0;
 }
 
