@@ -48,6 +48,9 @@ EDGE = [
             chunk_size=256, init_state=True, seed=25),
     _custom(name="f32_ragged", batch=2, seqlen=333, nheads=3, headdim=24, dstate=20, ngroups=3,
             chunk_size=32, dtype="f32", init_state=True, seed=26),
+    # float32 chunks too large for the LDS-staged kernels (the plain fallbacks)
+    _custom(name="f32_q256_fallback", batch=1, seqlen=600, nheads=2, headdim=32, dstate=64,
+            ngroups=1, chunk_size=256, dtype="f32", init_state=True, seed=28),
     _custom(name="L1", batch=1, seqlen=1, nheads=2, headdim=64, dstate=64, ngroups=1,
             chunk_size=64, init_state=True, seed=27),
 ]
