@@ -694,9 +694,23 @@ def cpu_baseline(inp, w, tokens_per_head):
     oracle.ssd_recurrence(o["x"], o["dt"], o["A"], o["B"], o["C"], o["D"], o["init_state"],
                           chunk_size=w.chunk_size, want_final=True)
     dt = time.perf_counter() - t0
+    # the oracle's independent chunked form on the same sample: per-chunk
+    # local states, the jump across chunks, outputs of each chunk restarted
+    # from its start state
+    import numpy as np
+    t1 = time.perf_counter()
+    cs, _ = oracle.chunk_cumsum(o["dt"], o["A"], w.chunk_size)
+    S = oracle.chunk_local_states(o["x"], o["dt"], o["A"], o["B"], chunk_size=w.chunk_size)
+    hs, _ = oracle.state_passing(S, np.exp2(cs[..., -1]), o["init_state"])
+    del S
+    oracle.chunk_outputs(o["x"], o["dt"], o["A"], o["B"], o["C"], o["D"], hs,
+                         chunk_size=w.chunk_size)
+    dt_chunked = time.perf_counter() - t1
     return {"value": w.batch * Ls / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": dt,
-            "sample": f"first {Ls} of {w.seqlen} tokens, all {w.nheads} heads, batch {w.batch}"}
+            "sample": f"first {Ls} of {w.seqlen} tokens, all {w.nheads} heads, batch {w.batch}",
+            "chunked_form": {"value": w.batch * Ls / dt_chunked, "unit": "tokens/s",
+                             "seconds": dt_chunked}}
 
 
 if __name__ == "__main__":
