@@ -52,13 +52,15 @@ SHAPES = [
     # N = 512: two launches over halves of the state columns
     _w("span_Q64_N512_G4_R4_ragged", 4096 - 19, 32, 512, 4, 64, Bn=4, seed=103),
     _w("span_Q256_N512_G3_K4", 3000, 96, 512, 3, 256, init=False, seed=104),
+    # N = 256, one head per workgroup, two workgroups per CU (three-buffer ring)
+    _w("span_Q64_N256_G2_R1_two_per_cu", 4096 - 3, 66, 256, 2, 64, seed=105),
 ]
 
 # (span length, heads per workgroup) each shape reaches on a 256-CU device
 EXPECT = {"span_Q64_N256_last_span_one_chunk": (4, 2), "span_Q64_N256_R4_ragged": (8, 4),
           "span_Q128_N128_G2_R2": (8, 2), "span_Q256_N64_G4_R1": (8, 1),
           "span_Q64_N64_R1_ragged": (8, 1), "span_Q64_N512_G4_R4_ragged": (8, 4),
-          "span_Q256_N512_G3_K4": (4, 1)}
+          "span_Q256_N512_G3_K4": (4, 1), "span_Q64_N256_G2_R1_two_per_cu": (8, 1)}
 
 
 def span_chunks(w, cus):
