@@ -62,7 +62,9 @@ struct SpanCfg {
   static constexpr int XS = R * XH;
   static constexpr int BS = RB * N * 2;      // B rows of a block, 2N bytes each
   static constexpr int CS = 1024;            // per head: 32 cumulative sums, 32 dt
-  static constexpr int CL = 256;             // per head: cs[Q-4 .. Q-1] of the block's chunk
+  // per head (16 bytes each): cs[Q-4 .. Q-1] of the block's chunk; sized for
+  // all 64 lanes of its load, so that load needs no lane mask
+  static constexpr int CL = 1024;
   static constexpr int BUF = XS + BS + CS + CL;
   // workgroups per CU: the target, if two buffers each still fit
   static constexpr int OCC = (160 * 1024 / (2 * BUF)) < OCCT ? (160 * 1024 / (2 * BUF)) : OCCT;
@@ -162,17 +164,21 @@ __device__ __forceinline__ void issue_block(uint32_t buf, const bf16* __restrict
 }
 
 // The same loads with the per-lane addresses formed once per workgroup: for
-// load slot j of this wave, the address of block 0 (p[j]) and the LDS offset
-// (dst[j]); block i's address is p[j] plus i times the slot's per-block
-// stride (per chunk for the last cumulative sums).  Valid while the block
-// lies inside the sequence (no clamping needed).
+// load slot j of this wave, the address of block 0 (p[j]), the LDS offset
+// (dst[j]) and the slot's strides per block and per chunk (the last
+// cumulative sums move once per chunk).  The slot's kind only decides those
+// values at set-up: every load is issued the same way, with all 64 lanes
+// (lanes past the heads load a valid duplicate into unused LDS), so issuing
+// a block takes no lane masks or branches on the kind.  Valid while the
+// block lies inside the sequence (no clamping needed).
 template <int Q, int N, int R, int LDN>
 struct DmaPlan {
   using C = SpanCfg<Q, N, R>;
   static constexpr int NJ = (C::TOT + C::NW - 1) / C::NW;
   const char* p[NJ];
   uint32_t dst[NJ];
-  int kind[NJ];  // 0 x, 1 B, 2 sums and dt, 3 last sums, -1 none
+  int64_t st[NJ], sc[NJ];
+  int nj;  // slots this wave issues
 
   __device__ __forceinline__ void init(const bf16* __restrict__ x, const bf16* __restrict__ Bm,
                                        const float* __restrict__ dA_cs,
@@ -181,55 +187,48 @@ struct DmaPlan {
     const int lane = lane_id();
     const int w = wave_id();
     const int64_t tok0 = (int64_t)c0 * Q;
+    nj = 0;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int k = j * C::NW + w;
-      kind[j] = -1;
       p[j] = (const char*)dA_cs;
       dst[j] = 0;
+      st[j] = sc[j] = 0;
+      if (k < C::TOT) nj = j + 1;
       if (k < C::XT) {
         const int r = k >> 2, s = (k & 3) * 64 + lane;
         const int row = s >> 3, pos = s & 7;
         p[j] = (const char*)(x + (((int64_t)b * L + tok0 + row) * H + h0 + r) * C::P + 8 * sx(row, pos));
         dst[j] = r * C::XH + (k & 3) * 1024;
-        kind[j] = 0;
+        st[j] = (int64_t)C::RB * H * C::P * 2;
       } else if (k < C::XT + C::BT) {
         const int s = (k - C::XT) * 64 + lane;
         const int row = s / (N / 8), pos = s % (N / 8);
         p[j] = (const char*)(Bm + (((int64_t)b * L + tok0 + row) * G + g) * LDN + ncol0 +
                              8 * sb<N>(row, pos));
         dst[j] = C::XS + (k - C::XT) * 1024;
-        kind[j] = 1;
+        st[j] = (int64_t)C::RB * G * LDN * 2;
       } else if (k == C::XT + C::BT) {
         const int r = lane >> 4, q = lane & 15;
         const int rr = r < R ? r : 0;
         const int64_t o = (((int64_t)b * H + h0 + rr) * nc + c0) * Q + 4 * (q & 7);
         p[j] = (const char*)((q < 8 ? dA_cs : dt_T) + o);
         dst[j] = C::XS + C::BS;
-        kind[j] = 2;
+        st[j] = (int64_t)C::RB * 4;
       } else if (k == C::XT + C::BT + 1) {
         const int rr = lane < R ? lane : 0;
         p[j] = (const char*)(dA_cs + (((int64_t)b * H + h0 + rr) * nc + c0) * Q + Q - 4);
         dst[j] = C::XS + C::BS + C::CS;
-        kind[j] = 3;
+        sc[j] = (int64_t)Q * 4;
       }
     }
   }
 
-  __device__ __forceinline__ void issue(uint32_t buf, int i, int H, int G) const {
-    const int lane = lane_id();
-    const int64_t xs = (int64_t)i * C::RB * H * C::P * 2;
-    const int64_t bstr = (int64_t)i * C::RB * G * LDN * 2;
-    const int64_t cstr = (int64_t)i * C::RB * 4;
-    const int64_t lstr = (int64_t)(i / C::BPC) * Q * 4;
+  __device__ __forceinline__ void issue(uint32_t buf, int i) const {
+    const int ic = i / C::BPC;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int kd = kind[j];
-      if (kd == 0) dma16(p[j] + xs, buf + dst[j]);
-      else if (kd == 1) dma16(p[j] + bstr, buf + dst[j]);
-      else if (kd == 2) { if ((lane >> 4) < R) dma16(p[j] + cstr, buf + dst[j] + lane * 16); }
-      else if (kd == 3) { if (lane < R) dma16(p[j] + lstr, buf + dst[j] + lane * 16); }
-    }
+    for (int j = 0; j < NJ; ++j)
+      if (j < nj) dma16(p[j] + i * st[j] + ic * sc[j], buf + dst[j]);
   }
 };
 
@@ -331,7 +330,7 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
 #pragma unroll
   for (int j = 0; j < C::NBUF - 1; ++j) {
     if (j < nfast)
-      plan.issue(sbase + j * C::BUF, j, H, G);
+      plan.issue(sbase + j * C::BUF, j);
     else if (j < nblk)
       issue_block<Q, N, R, LDN>(sbase + j * C::BUF, x, Bm, dA_cs, dt_T, c0 + j / C::BPC,
                                 j % C::BPC, b, h0, g, L, H, G, nc, ncol0);
@@ -390,7 +389,7 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
     if (i + C::NBUF - 1 < nblk) {
       const int j = i + C::NBUF - 1;
       if (j < nfast)
-        plan.issue(sbase + (j % C::NBUF) * C::BUF, j, H, G);
+        plan.issue(sbase + (j % C::NBUF) * C::BUF, j);
       else
         issue_block<Q, N, R, LDN>(sbase + (j % C::NBUF) * C::BUF, x, Bm, dA_cs, dt_T,
                                   c0 + j / C::BPC, j % C::BPC, b, h0, g, L, H, G, nc, ncol0);
