@@ -235,9 +235,10 @@ struct DmaPlan {
 // Which part of the run's states tile m of wave w holds: R tiles of 32 state
 // columns each (all 64 rows as 2 x 4 MFMA tiles).  With R <= NW the NW / R
 // waves of a head split its N columns, so a wave contracts one head's x rows.
-// More heads than waves (a wave holding R / NW heads whole) is supported for
-// every instantiation, though the host's head rule (at most 1 head per
-// workgroup at N = 64 and 2 at N = 128) no longer picks it.
+// More heads than waves (a wave holding R / NW heads whole) is supported by
+// these helpers, though the launchers instantiate only the head counts the
+// host's rule picks (at most 1 head per workgroup at N = 64, 2 at N = 128),
+// which never exceed the waves.
 template <int NW, int R>
 __device__ __forceinline__ int tile_head(int w, int m) {
   return NW >= R ? w / (NW / R) : w * (R / NW) + m / NW;
@@ -580,9 +581,14 @@ hipError_t launch_span_qn(const Dims& d, int K, const void* x, const void* B, co
   if (d.Q == QQ && d.N == NN)                                                              \
     return launch_span<QQ, NN, R, REPLAY, NN>(d, K, x, B, dA_cs, dt_T, span_states,         \
                                               span_decay, hst, 0, s);
-  M2_SPAN(64, 64) M2_SPAN(64, 128) M2_SPAN(64, 256)
-  M2_SPAN(128, 64) M2_SPAN(128, 128) M2_SPAN(128, 256)
-  M2_SPAN(256, 64) M2_SPAN(256, 128) M2_SPAN(256, 256)
+  // only the head counts span_heads can pick: 1 at N = 64, up to 2 at N = 128
+  if constexpr (R == 1) {
+    M2_SPAN(64, 64) M2_SPAN(128, 64) M2_SPAN(256, 64)
+  }
+  if constexpr (R <= 2) {
+    M2_SPAN(64, 128) M2_SPAN(128, 128) M2_SPAN(256, 128)
+  }
+  M2_SPAN(64, 256) M2_SPAN(128, 256) M2_SPAN(256, 256)
 #undef M2_SPAN
   // state size 512: two launches over halves of the state columns (each
   // column of the state evolves on its own)
