@@ -187,6 +187,17 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     ms = ev0.elapsed_time(ev1) / args.steps
 
+    # Per-step spread: 20 more steps, each bracketed by its own events on the
+    # launch stream (the events sit between steps, so the steps still run
+    # back to back); reported beside the mean, not used for `value`.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+    evs[0].record(stream)
+    for k in range(20):
+        step()
+        evs[k + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(20))
+
     # Per-stage durations of the same forward: HIP events recorded on the launch
     # stream between the four kernels (mamba2_ssd_forward_profile).
     stage_sum = [0.0] * 4
@@ -225,6 +236,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_spread": {"median": (per_step[9] + per_step[10]) / 2, "min": per_step[0],
+                               "max": per_step[-1], "steps": 20},
         "wall_ms_per_step": wall_ms,
         "higher_is_better": True,
         "scaling": "weak",
