@@ -21,7 +21,7 @@ namespace m2 {
 
 namespace {
 
-constexpr int kHeadTile = 16;
+constexpr int kHeadTile = 8;  // heads per workgroup: one 16-byte bf16 dt load per thread
 
 template <typename T>
 __device__ __forceinline__ float load_f32(const T* p);
