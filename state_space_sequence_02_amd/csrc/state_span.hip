@@ -276,18 +276,24 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
     const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ dA_cs,
     const float* __restrict__ dt_T, float* __restrict__ span_states,
     float* __restrict__ span_decay, bf16* __restrict__ hst, int L, int H, int G, int nc, int K,
-    int ng, int BNGG, int ncol0) {
+    int ng, int BNGG, int ncol0_arg) {
   // Rows of B, of the span states and of the chunk-start states hold LDN
-  // columns; this launch covers columns ncol0 .. ncol0 + N - 1.
+  // columns; a workgroup covers columns ncol0 .. ncol0 + N - 1 (ncol0_arg
+  // when there is one column half, from the workgroup id when two).
   using C = SpanCfg<Q, N, R, OCCT>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
-  // Every run of a (batch, span, group) on one XCD: id = 8 r + xcd,
-  // r = RG q + run, (batch, span, group) index 8 q + xcd.
+  // Every run of a (batch, span, group), and at LDN = 2N both column halves
+  // of it, on one XCD, so the span's B rows and x rows are fetched into that
+  // XCD's L2 once: id = 8 r + xcd, r = NH RG q + NH run + half,
+  // (batch, span, group) index 8 q + xcd.
+  constexpr int NH = LDN / N;
   const int HG = H / G, RG = HG / R;
   const int xcd = blockIdx.x & 7, rq = blockIdx.x >> 3;
-  const int run = rq % RG;
-  const int bsg = (rq / RG) * 8 + xcd;
+  const int rh = rq % (RG * NH);
+  const int run = rh / NH;
+  const int ncol0 = NH == 1 ? ncol0_arg : (rh % NH) * N;
+  const int bsg = (rq / (RG * NH)) * 8 + xcd;
   if (bsg >= BNGG) return;
   const int g = bsg % G;
   const int b = bsg / G / ng, s = (bsg / G) % ng;
@@ -531,7 +537,7 @@ int span_heads(const Dims& d, int K) {
 template <int Q, int N, int R, bool REPLAY, int LDN, int OCCT>
 hipError_t launch_span_occ(const Dims& d, int K, const void* x, const void* B,
                            const float* dA_cs, const float* dt_T, float* span_states,
-                           float* span_decay, void* hst, int ncol0, hipStream_t s) {
+                           float* span_decay, void* hst, hipStream_t s) {
   using C = SpanCfg<Q, N, R, OCCT>;
   auto kern = chunk_state_span_kernel<Q, N, R, REPLAY, LDN, OCCT>;
   static const hipError_t attr = hipFuncSetAttribute(
@@ -539,11 +545,11 @@ hipError_t launch_span_occ(const Dims& d, int K, const void* x, const void* B,
   if (attr != hipSuccess) return attr;
   const int64_t ng = (d.nc + K - 1) / K;
   const int64_t BNGG = d.B * ng * d.G;
-  const int64_t grid = (BNGG + 7) / 8 * 8 * (d.H / d.G / R);
+  const int64_t grid = (BNGG + 7) / 8 * 8 * (d.H / d.G / R) * (LDN / N);
   kern<<<(unsigned)grid, C::NT, C::LDS, s>>>((const bf16*)x, (const bf16*)B, dA_cs, dt_T,
                                            span_states, span_decay, (bf16*)hst, (int)d.L,
                                            (int)d.H, (int)d.G, (int)d.nc, K, (int)ng, (int)BNGG,
-                                           ncol0);
+                                           0);
   return hipGetLastError();
 }
 
@@ -555,22 +561,22 @@ hipError_t launch_span_occ(const Dims& d, int K, const void* x, const void* B,
 template <int Q, int N, int R, bool REPLAY, int LDN>
 hipError_t launch_span(const Dims& d, int K, const void* x, const void* B, const float* dA_cs,
                        const float* dt_T, float* span_states, float* span_decay, void* hst,
-                       int ncol0, hipStream_t s) {
+                       hipStream_t s) {
   if constexpr (kSpanOcc == 1 && (R == 1 || (N == 128 && R == 2))) {
     const int64_t ng = (d.nc + K - 1) / K;
-    const int64_t grid = (d.B * ng * d.G + 7) / 8 * 8 * (d.H / d.G / R);
+    const int64_t grid = (d.B * ng * d.G + 7) / 8 * 8 * (d.H / d.G / R) * (LDN / N);
     const int64_t cus = cu_count_span();
     if constexpr (N == 64) {
       if (grid > 2 * cus)
         return launch_span_occ<Q, N, R, REPLAY, LDN, 4>(d, K, x, B, dA_cs, dt_T, span_states,
-                                                        span_decay, hst, ncol0, s);
+                                                        span_decay, hst, s);
     }
     if (grid > cus)
       return launch_span_occ<Q, N, R, REPLAY, LDN, 2>(d, K, x, B, dA_cs, dt_T, span_states,
-                                                      span_decay, hst, ncol0, s);
+                                                      span_decay, hst, s);
   }
   return launch_span_occ<Q, N, R, REPLAY, LDN, kSpanOcc>(d, K, x, B, dA_cs, dt_T, span_states,
-                                                         span_decay, hst, ncol0, s);
+                                                         span_decay, hst, s);
 }
 
 template <int R, bool REPLAY>
@@ -580,7 +586,7 @@ hipError_t launch_span_qn(const Dims& d, int K, const void* x, const void* B, co
 #define M2_SPAN(QQ, NN)                                                                    \
   if (d.Q == QQ && d.N == NN)                                                              \
     return launch_span<QQ, NN, R, REPLAY, NN>(d, K, x, B, dA_cs, dt_T, span_states,         \
-                                              span_decay, hst, 0, s);
+                                              span_decay, hst, s);
   // only the head counts span_heads can pick: 1 at N = 64, up to 2 at N = 128
   if constexpr (R == 1) {
     M2_SPAN(64, 64) M2_SPAN(128, 64) M2_SPAN(256, 64)
@@ -590,17 +596,12 @@ hipError_t launch_span_qn(const Dims& d, int K, const void* x, const void* B, co
   }
   M2_SPAN(64, 256) M2_SPAN(128, 256) M2_SPAN(256, 256)
 #undef M2_SPAN
-  // state size 512: two launches over halves of the state columns (each
+  // state size 512: both halves of the state columns in one launch (each
   // column of the state evolves on its own)
 #define M2_SPAN512(QQ)                                                                       \
-  if (d.Q == QQ && d.N == 512) {                                                             \
-    const hipError_t e = launch_span<QQ, 256, R, REPLAY, 512>(d, K, x, B, dA_cs, dt_T,       \
-                                                              span_states, span_decay, hst, \
-                                                              0, s);                         \
-    if (e != hipSuccess) return e;                                                           \
+  if (d.Q == QQ && d.N == 512)                                                               \
     return launch_span<QQ, 256, R, REPLAY, 512>(d, K, x, B, dA_cs, dt_T, span_states,        \
-                                                span_decay, hst, 256, s);                    \
-  }
+                                                span_decay, hst, s);
   M2_SPAN512(64) M2_SPAN512(128) M2_SPAN512(256)
 #undef M2_SPAN512
   return hipErrorInvalidValue;
