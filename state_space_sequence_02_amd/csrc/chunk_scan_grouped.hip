@@ -310,7 +310,10 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
 
   // Head 0's bytes start flowing while G is formed.
   const uint32_t sbase = lds_addr(smem);
-  load_head<P, Q, N, MODE>(sbase, hst, x, dA_cs, dt_T, b, c, h0, L, H, nc, ldn, n0);
+  // each workgroup walks its heads from a different one, so the workgroups
+  // in flight touch different heads' slices of the token rows
+  const int rot = nh > 0 ? c % nh : 0;
+  load_head<P, Q, N, MODE>(sbase, hst, x, dA_cs, dt_T, b, c, h0 + rot, L, H, nc, ldn, n0);
 
   // ---- Phase A: G^T tiles of this wave's two i-tiles, and its C operands.
   // G^T tiles: j-tile jt of i-tile t0 in slot jt (jt <= t0), of i-tile t1 in
@@ -365,11 +368,12 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
 
   // ---- Phase B: heads.
   for (int k = 0; k < nh; ++k) {
-    const int h = h0 + k;
+    const int kr = k + rot < nh ? k + rot : k + rot - nh;
+    const int h = h0 + kr;
     unsigned char* cur = smem + (k & 1) * K::BUF;
     if (k + 1 < nh)
-      load_head<P, Q, N, MODE>(sbase + ((k + 1) & 1) * K::BUF, hst, x, dA_cs, dt_T, b, c, h + 1,
-                               L, H, nc, ldn, n0);
+      load_head<P, Q, N, MODE>(sbase + ((k + 1) & 1) * K::BUF, hst, x, dA_cs, dt_T, b, c,
+                               h0 + (kr + 1 < nh ? kr + 1 : kr + 1 - nh), L, H, nc, ldn, n0);
     const unsigned char* Hs = cur;
     const unsigned char* Xs = cur + K::HS_BYTES;
     const float* css = (const float*)(Xs + K::XS_BYTES);
