@@ -330,13 +330,17 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
     }
   };
 
-  issue(h0, 0);
-  load_x(h0);
+  // each workgroup walks its heads from a different one, so the workgroups
+  // in flight touch different heads' slices of the token rows
+  const int rot = c % nh;
+  const auto head_at = [&](int k) { return h0 + (k + rot < nh ? k + rot : k + rot - nh); };
+  issue(head_at(0), 0);
+  load_x(head_at(0));
   for (int hh = 0; hh < nh; ++hh) {
-    const int h = h0 + hh;
+    const int h = head_at(hh);
     __builtin_amdgcn_s_waitcnt(0);  // this head's buffer and x values landed
     __syncthreads();                // ... for every wave; the other buffer is free
-    if (hh + 1 < nh) issue(h + 1, (hh + 1) & 1);
+    if (hh + 1 < nh) issue(head_at(hh + 1), (hh + 1) & 1);
     const unsigned char* cur = smem + (hh & 1) * S::BUF;
     const bf16* Gs = (const bf16*)(cur + S::GS);
     const bf16* Ys = (const bf16*)(cur + S::YS);
@@ -428,7 +432,7 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
     const float Ah = A[h];
     dd = wave_sum(dd);
     if (lane == 0) red[w] = dd;
-    if (hh + 1 < nh) load_x(h + 1);
+    if (hh + 1 < nh) load_x(head_at(hh + 1));
     lds_barrier();  // LDS only: the loads in flight keep flying
 
     // ---- d(A dt)_k, ddt, and the dA and dD parts (one wave)

@@ -109,8 +109,11 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
   const int n0 = w * 16 * NTW;
   const int64_t tok0 = (int64_t)c * Q;
 
+  // each workgroup walks its heads from a different one, so the workgroups
+  // in flight touch different heads' slices of the token rows
+  const int rot = nh > 0 ? c % nh : 0;
   const uint32_t sbase = lds_addr(smem);
-  load_x<P, Q, N>(sbase, x, dA_cs, dt_T, b, c, h0, L, H, nc);
+  load_x<P, Q, N>(sbase, x, dA_cs, dt_T, b, c, h0 + rot, L, H, nc);
 
   // ---- Phase A: B^T operands of this wave's columns, 64 time steps at a time.
   bf16x8 Bop[NTW][KS];
@@ -145,9 +148,12 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
 
   // ---- Phase B: heads.
   for (int k = 0; k < nh; ++k) {
-    const int h = h0 + k;
+    const int kr = k + rot < nh ? k + rot : k + rot - nh;
+    const int h = h0 + kr;
     unsigned char* cur = smem + (k & 1) * K::BUF;
-    if (k + 1 < nh) load_x<P, Q, N>(sbase + ((k + 1) & 1) * K::BUF, x, dA_cs, dt_T, b, c, h + 1, L, H, nc);
+    if (k + 1 < nh)
+      load_x<P, Q, N>(sbase + ((k + 1) & 1) * K::BUF, x, dA_cs, dt_T, b, c,
+                      h0 + (kr + 1 < nh ? kr + 1 : kr + 1 - nh), L, H, nc);
     // Scale x rows by w_j in place (each 16-byte slot belongs to row s / 8).
     {
       const float* css = (const float*)(cur + K::XS_BYTES);
