@@ -311,8 +311,9 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
   // Head 0's bytes start flowing while G is formed.
   const uint32_t sbase = lds_addr(smem);
   // each workgroup walks its heads from a different one, so the workgroups
-  // in flight touch different heads' slices of the token rows
-  const int rot = nh > 0 ? c % nh : 0;
+  // in flight touch different heads' slices of the token rows; the c / 8
+  // term spreads the start heads of one XCD's chunks (c = XCD mod 8) too
+  const int rot = nh > 0 ? (c + (c >> 3)) % nh : 0;
   load_head<P, Q, N, MODE>(sbase, hst, x, dA_cs, dt_T, b, c, h0 + rot, L, H, nc, ldn, n0);
 
   // ---- Phase A: G^T tiles of this wave's two i-tiles, and its C operands.
