@@ -110,8 +110,9 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
   const int64_t tok0 = (int64_t)c * Q;
 
   // each workgroup walks its heads from a different one, so the workgroups
-  // in flight touch different heads' slices of the token rows
-  const int rot = nh > 0 ? c % nh : 0;
+  // in flight touch different heads' slices of the token rows; the c / 8
+  // term spreads the start heads of one XCD's chunks (c = XCD mod 8) too
+  const int rot = nh > 0 ? (c + (c >> 3)) % nh : 0;
   const uint32_t sbase = lds_addr(smem);
   load_x<P, Q, N>(sbase, x, dA_cs, dt_T, b, c, h0 + rot, L, H, nc);
 
