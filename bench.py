@@ -140,13 +140,13 @@ def main():
         return
     if args.backward:
         if args.gpus != 1:
-            print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+            print(json.dumps({"error": "this benchmark runs on one GPU only; run with --gpus 1",
                               "n_gpus": args.gpus}))
             sys.exit(2)
         backward_bench(args)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.state_path == "fused":
@@ -421,7 +421,7 @@ def sweep_bench(args):
     against 8 TB/s; MFMA is the algorithmic flops over the step time against
     the dense bf16 peak."""
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
