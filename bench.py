@@ -174,6 +174,19 @@ def main():
         m2.mamba2_ssd_forward(dims, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"],
                               g["init_state"], y, fin, ws, need, stream)
 
+    # Per-stage durations of the same forward first: HIP events recorded on the
+    # launch stream between its kernels (mamba2_ssd_forward_profile), at least
+    # 50 calls and 0.25 s.  This also brings the GPU's clocks to their steady
+    # state before the warm-up and timed steps below (they take tens of
+    # milliseconds of load to settle).
+    stage_sum, n_prof = [0.0] * 4, 0
+    t_prof = time.perf_counter()
+    while n_prof < 50 or time.perf_counter() - t_prof < 0.25:
+        ms4 = m2.mamba2_ssd_forward_profile(dims, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"],
+                                            g["init_state"], y, fin, ws, need, stream)
+        stage_sum = [a + b for a, b in zip(stage_sum, ms4)]
+        n_prof += 1
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -198,16 +211,9 @@ def main():
     torch.cuda.synchronize()
     per_step = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(20))
 
-    # Per-stage durations of the same forward: HIP events recorded on the launch
-    # stream between the four kernels (mamba2_ssd_forward_profile).
-    stage_sum = [0.0] * 4
-    for _ in range(args.steps):
-        ms4 = m2.mamba2_ssd_forward_profile(dims, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"],
-                                            g["init_state"], y, fin, ws, need, stream)
-        stage_sum = [a + b for a, b in zip(stage_sum, ms4)]
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     names = forward_stages(w, cus)
-    stage_ms = {s: stage_sum[i] / args.steps for i, s in enumerate(names)}
+    stage_ms = {s: stage_sum[i] / n_prof for i, s in enumerate(names)}
     model = stage_model(w, cus)
     dom = max(names, key=lambda s: stage_ms[s])
     dm = model[dom]
@@ -250,12 +256,53 @@ def main():
         "roofline": {"kernel": dom, "bound": bound, "achieved": achieved, "peak": peak,
                      "unit": unit, "frac": achieved / peak,
                      "traffic": profiled_traffic(w.name, dom),
-                     "algorithmic_bytes": dm["bytes"], "algorithmic_flops": dm["flops"]},
+                     "algorithmic_bytes": dm["bytes"], "algorithmic_flops": dm["flops"],
+                     "mfma": mfma_fractions(w, dom, stage_ms[dom])},
         "stages": stages,
+        "stage_timing_calls": n_prof,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_tokens)
     print(json.dumps(out), flush=True)
+
+
+def effective_flops(w, stage):
+    """Flops of `stage` counted per head, as a kernel that did not share the
+    group's C B^T across heads would execute them: 4NP + (Q+1)(N+P) + 2P per
+    (token, head) for the whole forward, of which the output stage's share is
+    2NP + (Q+1)(N+P) + 2P.  Other stages have nothing shared, so their count
+    equals the issued one."""
+    B, L, H, P, N, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk_size
+    tok = B * L
+    if stage == "chunk_scan":
+        return tok * H * (2 * N * P + (Q + 1) * (N + P) + 2 * P)
+    return stage_model(w)[stage]["flops"]
+
+
+def mfma_fractions(w, stage, ms):
+    """The dominant kernel against the dense bf16 MFMA peak, both ways:
+    issued = the flops the kernel performs (C B^T once per (chunk, group)),
+    effective = the per-head count of the same work."""
+    issued = stage_model(w)[stage]["flops"]
+    eff = effective_flops(w, stage)
+    t = ms * 1e-3
+    return {"issued_flops": issued, "issued_TFLOP/s": issued / t / 1e12,
+            "issued_frac": issued / t / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "effective_flops": eff, "effective_TFLOP/s": eff / t / 1e12,
+            "effective_frac": eff / t / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "peak_TFLOP/s": BF16_MFMA_PEAK_TFLOPS}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def fused_state_model(w):
@@ -567,7 +614,7 @@ def decode_cpu_baseline(inp, w):
         if sec >= 1.0:
             break
     return {"value": w.batch * reps / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": sec,
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": sec,
             "sample": f"{reps} one-token steps of the whole batch ({w.batch} sequences, "
                       f"{w.nheads} heads)"}
 
@@ -691,7 +738,7 @@ def backward_bench(args):
         sec = time.perf_counter() - t0
         out["cpu_baseline"] = {
             "value": w.batch * Ls / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": sec,
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": sec,
             "sample": f"first {Ls} of {w.seqlen} tokens, all {w.nheads} heads, batch {w.batch}"}
     print(json.dumps(out), flush=True)
 
@@ -720,7 +767,7 @@ def cpu_baseline(inp, w, tokens_per_head):
                          chunk_size=w.chunk_size)
     dt_chunked = time.perf_counter() - t1
     return {"value": w.batch * Ls / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": dt,
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": dt,
             "sample": f"first {Ls} of {w.seqlen} tokens, all {w.nheads} heads, batch {w.batch}",
             "chunked_form": {"value": w.batch * Ls / dt_chunked, "unit": "tokens/s",
                              "seconds": dt_chunked}}

@@ -13,6 +13,14 @@ current torch stream into a ``hipStream_t``.  The functions keep the C names:
 plus ``make_dims`` and ``ssd_forward`` (allocates outputs and workspace with
 torch, then calls ``mamba2_ssd_forward``).  Importing fails loudly when the
 library has not been built; there is no fallback implementation.
+
+The C ABI receives bare pointers and can only check them for NULL and
+alignment, so every wrapper here checks each torch tensor against the sizes
+in ``dims`` first: dtype (x, dt, B, C, y and their gradients in the dims
+dtype; A, D, states, sums and every state-shaped tensor float32), shape,
+contiguity and that it lives on a GPU, raising ``Mamba2Error`` with
+``MAMBA2_ERR_DTYPE``, ``MAMBA2_ERR_SHAPE`` or ``MAMBA2_ERR_NULL`` before any
+call.  A plain ``int`` is taken as a raw device address and passed as is.
 """
 from __future__ import annotations
 
@@ -58,9 +66,11 @@ class Mamba2Dims(ctypes.Structure):
 
 
 class Mamba2Error(RuntimeError):
-    def __init__(self, status: int, where: str):
+    def __init__(self, status: int, where: str, detail: str | None = None):
         self.status = status
-        super().__init__(f"{where}: {mamba2_status_string(status)} ({mamba2_last_error()})")
+        if detail is None:
+            detail = mamba2_last_error()
+        super().__init__(f"{where}: {mamba2_status_string(status)} ({detail})")
 
 
 def _load():
@@ -122,6 +132,77 @@ def _check(status: int, where: str):
         raise Mamba2Error(status, where)
 
 
+def _io_dtype(dims):
+    return torch.float32 if dims.dtype == MAMBA2_DTYPE_F32 else torch.bfloat16
+
+
+def _nchunks(dims):
+    return -(-dims.seqlen // dims.chunk_size)
+
+
+def _shapes(dims):
+    """Expected (shape, dtype) of every tensor role for these dims."""
+    b, L, H, P, N, G = (dims.batch, dims.seqlen, dims.nheads, dims.headdim, dims.dstate,
+                        dims.ngroups)
+    nc, Q, io, f = _nchunks(dims), dims.chunk_size, _io_dtype(dims), torch.float32
+    return {
+        "x": ((b, L, H, P), io), "y": ((b, L, H, P), io), "dt": ((b, L, H), io),
+        "A": ((H,), f), "D": ((H,), f), "B": ((b, L, G, N), io), "C": ((b, L, G, N), io),
+        "state": ((b, H, P, N), f), "sums": ((b, H, nc, Q), f),
+        "states": ((b, nc, H, P, N), f), "start_bf16": ((b, nc, H, P, N), torch.bfloat16),
+        # one-token step: the sequence axis is absent
+        "x1": ((b, H, P), io), "dt1": ((b, H), io), "B1": ((b, G, N), io),
+    }
+
+
+def _req(where, dims, role, name, t, optional=False):
+    """Checks one argument: None only if optional; an int passes as a raw
+    device address; a tensor must match its role's dtype and shape and be
+    contiguous (the device is checked for all arguments at once, after)."""
+    if t is None:
+        if optional:
+            return
+        raise Mamba2Error(MAMBA2_ERR_NULL, where, f"{name} is None")
+    if isinstance(t, int):
+        return
+    if not isinstance(t, torch.Tensor):
+        raise Mamba2Error(MAMBA2_ERR_SHAPE, where, f"{name} is a {type(t).__name__}, not a tensor")
+    shape, dtype = _shapes(dims)[role]
+    if t.dtype != dtype:
+        raise Mamba2Error(MAMBA2_ERR_DTYPE, where, f"{name} is {t.dtype}, needs {dtype}")
+    if tuple(t.shape) != shape:
+        raise Mamba2Error(MAMBA2_ERR_SHAPE, where,
+                          f"{name} has shape {tuple(t.shape)}, needs {shape}")
+    if not t.is_contiguous():
+        raise Mamba2Error(MAMBA2_ERR_SHAPE, where,
+                          f"{name} is not contiguous (strides {t.stride()})")
+
+
+def _req_bytes(where, name, t, nbytes):
+    """A workspace: raw address, or a contiguous GPU tensor of at least nbytes."""
+    if t is None:
+        raise Mamba2Error(MAMBA2_ERR_WORKSPACE, where, f"{name} is None")
+    if isinstance(t, int):
+        return
+    if not t.is_contiguous():
+        raise Mamba2Error(MAMBA2_ERR_WORKSPACE, where, f"{name} is not contiguous")
+    if t.numel() * t.element_size() < int(nbytes):
+        raise Mamba2Error(MAMBA2_ERR_WORKSPACE, where,
+                          f"{name} holds {t.numel() * t.element_size()} bytes, "
+                          f"{int(nbytes)} passed")
+
+
+def _same_device(where, *ts):
+    """After the per-tensor checks: every tensor on one GPU."""
+    devs = {t.device for t in ts if isinstance(t, torch.Tensor)}
+    off = sorted(str(d) for d in devs if d.type != "cuda")
+    if off:
+        raise Mamba2Error(MAMBA2_ERR_NULL, where, f"tensors on {off}, not on a GPU")
+    if len(devs) > 1:
+        raise Mamba2Error(MAMBA2_ERR_NULL, where,
+                          f"tensors on different GPUs: {sorted(map(str, devs))}")
+
+
 def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype) -> Mamba2Dims:
     """dtype: torch.float32 / torch.bfloat16 or the MAMBA2_DTYPE_* code."""
     if dtype is torch.float32:
@@ -132,9 +213,18 @@ def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype
 
 
 def dims_of(x: torch.Tensor, B: torch.Tensor, chunk_size: int) -> Mamba2Dims:
-    """Dims from x[B,L,H,P] and B[B,L,G,N]."""
+    """Dims from x[B,L,H,P] and B[B,L,G,N] (the dtype is x's: float32 or
+    bfloat16; every other tensor is then checked against these dims)."""
+    if x.dim() != 4 or B.dim() != 4:
+        raise Mamba2Error(MAMBA2_ERR_SHAPE, "dims_of",
+                          f"x {tuple(x.shape)} and B {tuple(B.shape)} must both be 4-d")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise Mamba2Error(MAMBA2_ERR_DTYPE, "dims_of", f"x is {x.dtype}, needs float32 or bfloat16")
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
+    if tuple(B.shape[:2]) != (b, L):
+        raise Mamba2Error(MAMBA2_ERR_SHAPE, "dims_of",
+                          f"B {tuple(B.shape)} does not match x {tuple(x.shape)} in batch/seqlen")
     return make_dims(b, L, H, P, N, G, chunk_size, x.dtype)
 
 
@@ -155,29 +245,65 @@ def mamba2_ssd_workspace_bytes(dims) -> int:
 
 
 def mamba2_chunk_cumsum(dims, dt, A, dA_cs, dt_T, stream=None):
+    w = "mamba2_chunk_cumsum"
+    for role, name, t in (("dt", "dt", dt), ("A", "A", A), ("sums", "dA_cs", dA_cs),
+                          ("sums", "dt_T", dt_T)):
+        _req(w, dims, role, name, t)
+    _same_device(w, dt, A, dA_cs, dt_T)
     _check(_lib.mamba2_chunk_cumsum(ctypes.byref(dims), _ptr(dt), _ptr(A), _ptr(dA_cs),
                                     _ptr(dt_T), _stream(stream)), "mamba2_chunk_cumsum")
 
 
 def mamba2_chunk_state(dims, x, B, dA_cs, dt_T, states, stream=None):
+    w = "mamba2_chunk_state"
+    for role, name, t in (("x", "x", x), ("B", "B", B), ("sums", "dA_cs", dA_cs),
+                          ("sums", "dt_T", dt_T), ("states", "states", states)):
+        _req(w, dims, role, name, t)
+    _same_device(w, x, B, dA_cs, dt_T, states)
     _check(_lib.mamba2_chunk_state(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(dA_cs), _ptr(dt_T),
                                    _ptr(states), _stream(stream)), "mamba2_chunk_state")
 
 
 def mamba2_state_passing(dims, states, dA_cs, init_state, final_state, stream=None):
+    w = "mamba2_state_passing"
+    _req(w, dims, "states", "states", states)
+    _req(w, dims, "sums", "dA_cs", dA_cs)
+    _req(w, dims, "state", "init_state", init_state, optional=True)
+    _req(w, dims, "state", "final_state", final_state, optional=True)
+    _same_device(w, states, dA_cs, init_state, final_state)
     _check(_lib.mamba2_state_passing(ctypes.byref(dims), _ptr(states), _ptr(dA_cs),
                                      _ptr(init_state), _ptr(final_state), _stream(stream)),
            "mamba2_state_passing")
 
 
 def mamba2_chunk_scan(dims, x, B, C, dA_cs, dt_T, states, D, y, stream=None):
+    w = "mamba2_chunk_scan"
+    for role, name, t in (("x", "x", x), ("B", "B", B), ("C", "C", C), ("sums", "dA_cs", dA_cs),
+                          ("sums", "dt_T", dt_T), ("states", "states", states), ("y", "y", y)):
+        _req(w, dims, role, name, t)
+    _req(w, dims, "D", "D", D, optional=True)
+    _same_device(w, x, B, C, dA_cs, dt_T, states, D, y)
     _check(_lib.mamba2_chunk_scan(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(C), _ptr(dA_cs),
                                   _ptr(dt_T), _ptr(states), _ptr(D), _ptr(y), _stream(stream)),
            "mamba2_chunk_scan")
 
 
+def _forward_args(w, dims, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                  workspace_bytes):
+    for role, name, t in (("x", "x", x), ("dt", "dt", dt), ("A", "A", A), ("B", "B", B),
+                          ("C", "C", C), ("y", "y", y)):
+        _req(w, dims, role, name, t)
+    _req(w, dims, "D", "D", D, optional=True)
+    _req(w, dims, "state", "init_state", init_state, optional=True)
+    _req(w, dims, "state", "final_state", final_state, optional=True)
+    _req_bytes(w, "workspace", workspace, workspace_bytes)
+    _same_device(w, x, dt, A, B, C, D, init_state, y, final_state, workspace)
+
+
 def mamba2_ssd_forward(dims, x, dt, A, B, C, D, init_state, y, final_state, workspace,
                        workspace_bytes, stream=None):
+    _forward_args("mamba2_ssd_forward", dims, x, dt, A, B, C, D, init_state, y, final_state,
+                  workspace, workspace_bytes)
     _check(_lib.mamba2_ssd_forward(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                    _ptr(C), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
                                    _ptr(workspace), int(workspace_bytes), _stream(stream)),
@@ -188,6 +314,8 @@ def mamba2_ssd_forward_profile(dims, x, dt, A, B, C, D, init_state, y, final_sta
                                workspace_bytes, stream=None):
     """Runs mamba2_ssd_forward, waits, and returns the four stage durations in ms
     (chunk_cumsum, chunk_state, state_passing, chunk_scan)."""
+    _forward_args("mamba2_ssd_forward_profile", dims, x, dt, A, B, C, D, init_state, y,
+                  final_state, workspace, workspace_bytes)
     ms = (ctypes.c_float * 4)()
     _check(_lib.mamba2_ssd_forward_profile(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A),
                                            _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), _ptr(y),
@@ -199,6 +327,14 @@ def mamba2_ssd_forward_profile(dims, x, dt, A, B, C, D, init_state, y, final_sta
 
 def mamba2_fwd_pass_state(dims, x, B, dA_cs, dt_T, init_state, w_T, chunk_start_states,
                           final_state, stream=None):
+    w = "mamba2_fwd_pass_state"
+    for role, name, t in (("x", "x", x), ("B", "B", B), ("sums", "dA_cs", dA_cs),
+                          ("sums", "dt_T", dt_T), ("sums", "w_T", w_T),
+                          ("start_bf16", "chunk_start_states", chunk_start_states),
+                          ("state", "final_state", final_state)):
+        _req(w, dims, role, name, t)
+    _req(w, dims, "state", "init_state", init_state, optional=True)
+    _same_device(w, x, B, dA_cs, dt_T, init_state, w_T, chunk_start_states, final_state)
     _check(_lib.mamba2_fwd_pass_state(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(dA_cs),
                                       _ptr(dt_T), _ptr(init_state), _ptr(w_T),
                                       _ptr(chunk_start_states), _ptr(final_state),
@@ -208,6 +344,8 @@ def mamba2_fwd_pass_state(dims, x, B, dA_cs, dt_T, init_state, w_T, chunk_start_
 
 def mamba2_ssd_forward_fused(dims, x, dt, A, B, C, D, init_state, y, final_state, workspace,
                              workspace_bytes, stream=None):
+    _forward_args("mamba2_ssd_forward_fused", dims, x, dt, A, B, C, D, init_state, y,
+                  final_state, workspace, workspace_bytes)
     _check(_lib.mamba2_ssd_forward_fused(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                          _ptr(C), _ptr(D), _ptr(init_state), _ptr(y),
                                          _ptr(final_state), _ptr(workspace),
@@ -216,6 +354,12 @@ def mamba2_ssd_forward_fused(dims, x, dt, A, B, C, D, init_state, y, final_state
 
 
 def mamba2_decode_step(dims, x, dt, A, B, C, D, state, y, stream=None):
+    w = "mamba2_decode_step"
+    for role, name, t in (("x1", "x", x), ("dt1", "dt", dt), ("A", "A", A), ("B1", "B", B),
+                          ("B1", "C", C), ("state", "state", state), ("x1", "y", y)):
+        _req(w, dims, role, name, t)
+    _req(w, dims, "D", "D", D, optional=True)
+    _same_device(w, x, dt, A, B, C, D, state, y)
     _check(_lib.mamba2_decode_step(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                    _ptr(C), _ptr(D), _ptr(state), _ptr(y), _stream(stream)),
            "mamba2_decode_step")
@@ -224,6 +368,9 @@ def mamba2_decode_step(dims, x, dt, A, B, C, D, state, y, stream=None):
 def decode_step(x, dt, A, B, C, D, state, *, chunk_size=64, stream=None):
     """One token per (batch, head): x[B,H,P], dt[B,H], B/C[B,G,N]; updates the
     float32 state[B,H,P,N] in place and returns y[B,H,P] (allocated with torch)."""
+    if x.dim() != 3 or B.dim() != 3:
+        raise Mamba2Error(MAMBA2_ERR_SHAPE, "decode_step",
+                          f"x {tuple(x.shape)} and B {tuple(B.shape)} must both be 3-d")
     b, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
     dims = make_dims(b, 1, H, P, N, G, chunk_size, x.dtype)
@@ -255,7 +402,17 @@ def mamba2_ssd_backward_workspace_bytes(dims) -> int:
 
 
 def _bwd_args(dims, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB, dC, dD, dinit,
-              workspace, workspace_bytes):
+              workspace, workspace_bytes, where="mamba2_ssd_backward"):
+    for role, name, t in (("x", "x", x), ("dt", "dt", dt), ("A", "A", A), ("B", "B", B),
+                          ("C", "C", C), ("y", "dy", dy), ("x", "dx", dx), ("dt", "ddt", ddt),
+                          ("A", "dA", dA), ("B", "dB", dB), ("C", "dC", dC)):
+        _req(where, dims, role, name, t)
+    for role, name, t in (("D", "D", D), ("state", "init_state", init_state),
+                          ("state", "dfinal", dfinal), ("D", "dD", dD), ("state", "dinit", dinit)):
+        _req(where, dims, role, name, t, optional=True)
+    _req_bytes(where, "workspace", workspace, workspace_bytes)
+    _same_device(where, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB, dC, dD, dinit,
+                 workspace)
     return (ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
             _ptr(init_state), _ptr(dy), _ptr(dfinal), _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB),
             _ptr(dC), _ptr(dD), _ptr(dinit), _ptr(workspace), int(workspace_bytes))
@@ -275,7 +432,8 @@ def mamba2_ssd_backward_profile(dims, x, dt, A, B, C, D, init_state, dy, dfinal,
     ms = (ctypes.c_float * 8)()
     _check(_lib.mamba2_ssd_backward_profile(*_bwd_args(dims, x, dt, A, B, C, D, init_state, dy,
                                                        dfinal, dx, ddt, dA, dB, dC, dD, dinit,
-                                                       workspace, workspace_bytes),
+                                                       workspace, workspace_bytes,
+                                                       "mamba2_ssd_backward_profile"),
                                             _stream(stream), ms),
            "mamba2_ssd_backward_profile")
     return [float(v) for v in ms]

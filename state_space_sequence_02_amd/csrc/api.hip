@@ -56,12 +56,13 @@ int validate(const mamba2_dims* d, m2::Dims* out) {
     if (Q != 64 && Q != 128 && Q != 256)
       return fail(MAMBA2_ERR_UNSUPPORTED, "bfloat16 chunk_size must be 64, 128 or 256 (got %lld)",
                   (long long)Q);
-    if (d->headdim != 32 && d->headdim != 64 && d->headdim != 128)
-      return fail(MAMBA2_ERR_UNSUPPORTED, "bfloat16 headdim must be 32, 64 or 128 (got %lld)",
-                  (long long)d->headdim);
-    if (d->dstate % 64 != 0 || d->dstate > 512)
+    if (d->headdim % 16 != 0 || d->headdim > 128)
       return fail(MAMBA2_ERR_UNSUPPORTED,
-                  "bfloat16 dstate must be a multiple of 64 and at most 512 (got %lld)",
+                  "bfloat16 headdim must be a multiple of 16 and at most 128 (got %lld)",
+                  (long long)d->headdim);
+    if (d->dstate % 16 != 0 || d->dstate > 512)
+      return fail(MAMBA2_ERR_UNSUPPORTED,
+                  "bfloat16 dstate must be a multiple of 16 and at most 512 (got %lld)",
                   (long long)d->dstate);
   } else {
     if (Q != 16 && Q != 32 && Q != 64 && Q != 128 && Q != 256)

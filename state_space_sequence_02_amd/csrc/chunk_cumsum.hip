@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(256) chunk_cumsum_kernel(const T* __restrict__
   if (i < Q && t < L) {
     const T* src = dt + ((int64_t)b * L + t) * H + h0;
     constexpr int VE = Vec16<T>::n;
-    if (H % VE == 0) {  // h0 is a multiple of 16, so every vector is aligned
+    if (H % VE == 0) {  // h0 is a multiple of the head tile (8), so of VE: every vector is aligned
 #pragma unroll
       for (int k0 = 0; k0 < kHeadTile; k0 += VE) {
         if (k0 < nh) {

@@ -96,15 +96,25 @@ __device__ __forceinline__ void tile_out(f32x4 (&Gt)[NG], f32x4 (&Yt)[P / 16], i
   }
   if (i < valid) {
     bf16* dst = y + (ybase + (int64_t)i * H) * P + 4 * PT * grp;
+    if constexpr (PT % 2 == 0) {  // 16-byte stores
 #pragma unroll
-    for (int pt = 0; pt < PT; pt += 2) {
-      bf16x8 o;
+      for (int pt = 0; pt < PT; pt += 2) {
+        bf16x8 o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        o[r] = f2bf(Yt[pt][r]);
-        o[4 + r] = f2bf(Yt[pt + 1][r]);
+        for (int r = 0; r < 4; ++r) {
+          o[r] = f2bf(Yt[pt][r]);
+          o[4 + r] = f2bf(Yt[pt + 1][r]);
+        }
+        *(bf16x8*)(dst + 4 * pt) = o;
       }
-      *(bf16x8*)(dst + 4 * pt) = o;
+    } else {  // an odd tile count leaves the lane's run 8-byte aligned only
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = f2bf(Yt[pt][r]);
+        *(bf16x4*)(dst + 4 * pt) = o;
+      }
     }
   }
 }
@@ -165,6 +175,8 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_bf16_kernel(
 #pragma unroll
   for (int a = 0; a < PT; ++a) Y[0][a] = Y[1][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // State columns in blocks of NB; a last block reaching past N (N is a
+  // multiple of 16) is zero beyond it in all three tiles, so it adds nothing.
   const float* hsrc = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
   for (int nb = 0; nb < N; nb += NB) {
     __syncthreads();
@@ -172,7 +184,7 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_bf16_kernel(
       const int r = idx / (NB / 8), c8 = (idx % (NB / 8)) * 8;
       const int64_t t = tok0 + r;
       bf16x8 vc, vb;
-      if (t < L) {
+      if (t < L && nb + c8 < N) {
         const int64_t off = (((int64_t)b * L + t) * G + g) * N + nb + c8;
         vc = *(const bf16x8*)(Cm + off);
         vb = *(const bf16x8*)(Bm + off);
@@ -185,7 +197,8 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_bf16_kernel(
     }
     for (int idx = tid; idx < P * (NB / 4); idx += nthr) {
       const int p = idx / (NB / 4), c4 = (idx % (NB / 4)) * 4;
-      const f32x4 v = *(const f32x4*)(hsrc + (int64_t)p * N + nb + c4);
+      const f32x4 v = nb + c4 < N ? *(const f32x4*)(hsrc + (int64_t)p * N + nb + c4)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
       bf16x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = f2bf(v[e]);
@@ -365,8 +378,13 @@ hipError_t launch_chunk_scan(const Dims& d, const void* x, const void* B, const 
                              const float* D, void* y, hipStream_t s) {
   if (d.bf16) {
     switch (d.P) {
+      case 16: return launch_bf16_q<16>(d, x, B, C, dA_cs, dt_T, states, D, y, s);
       case 32: return launch_bf16_q<32>(d, x, B, C, dA_cs, dt_T, states, D, y, s);
+      case 48: return launch_bf16_q<48>(d, x, B, C, dA_cs, dt_T, states, D, y, s);
       case 64: return launch_bf16_q<64>(d, x, B, C, dA_cs, dt_T, states, D, y, s);
+      case 80: return launch_bf16_q<80>(d, x, B, C, dA_cs, dt_T, states, D, y, s);
+      case 96: return launch_bf16_q<96>(d, x, B, C, dA_cs, dt_T, states, D, y, s);
+      case 112: return launch_bf16_q<112>(d, x, B, C, dA_cs, dt_T, states, D, y, s);
       case 128: return launch_bf16_q<128>(d, x, B, C, dA_cs, dt_T, states, D, y, s);
       default: return hipErrorInvalidValue;
     }

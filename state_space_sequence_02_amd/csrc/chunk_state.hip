@@ -28,15 +28,18 @@ constexpr int kJB = 64;    // time steps staged per block
 constexpr int kXPad = 8;   // LDS row padding (elements)
 constexpr int kBPad = 8;
 
+// N is any multiple of 16: the waves cover Npad columns (N rounded up to the
+// waves' 16 NTW-column tiles); B columns past N are zero in LDS and their
+// state columns are not stored.
 template <int P, int NTW>
 __global__ void __launch_bounds__(1024) chunk_state_bf16_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ dA_cs,
-    const float* __restrict__ dt_T, float* __restrict__ states, int L, int H, int G, int N, int Q,
-    int nc) {
+    const float* __restrict__ dt_T, float* __restrict__ states, int L, int H, int G, int N,
+    int Npad, int Q, int nc) {
   constexpr int PT = P / 16;
   constexpr int XS = P + kXPad;  // LDS row stride of Xs (elements)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int BS = N + kBPad;
+  const int BS = Npad + kBPad;
   bf16* Xs = (bf16*)smem;                  // [kJB][XS]
   bf16* Bs = Xs + kJB * XS;                // [kJB][BS]
   float* wq = (float*)(Bs + kJB * BS);     // [Q]
@@ -84,13 +87,13 @@ __global__ void __launch_bounds__(1024) chunk_state_bf16_kernel(
       }
       *(bf16x8*)(Xs + r * XS + c8) = v;
     }
-    // Stage B rows: kJB x N.
-    const int nch = N / 8;
+    // Stage B rows: kJB x Npad (zero past N).
+    const int nch = Npad / 8;
     for (int idx = tid; idx < kJB * nch; idx += nthr) {
       const int r = idx / nch, c8 = (idx % nch) * 8;
       const int64_t t = t0 + jb + r;
       bf16x8 v;
-      if (t < L) {
+      if (t < L && c8 < N) {
         v = *(const bf16x8*)(Bm + ((((int64_t)b * L + t) * G + g) * N + c8));
       } else {
 #pragma unroll
@@ -122,11 +125,13 @@ __global__ void __launch_bounds__(1024) chunk_state_bf16_kernel(
 
   // acc[nt][pt][r] = S[p = 16 pt + L16][n = n0 + 4 NTW grp + 4 nt + r]
   float* out = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+  const int nl = n0 + 4 * NTW * grp;
 #pragma unroll
   for (int pt = 0; pt < PT; ++pt) {
-    float* row = out + (int64_t)(16 * pt + L16) * N + n0 + 4 * NTW * grp;
+    float* row = out + (int64_t)(16 * pt + L16) * N + nl;
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) *(f32x4*)(row + 4 * nt) = acc[nt][pt];
+    for (int nt = 0; nt < NTW; ++nt)
+      if (nl + 4 * nt < N) *(f32x4*)(row + 4 * nt) = acc[nt][pt];
   }
 }
 
@@ -207,8 +212,11 @@ size_t f32_state_lds_bytes(const Dims& d) {
 template <int P, int NTW>
 hipError_t launch_bf16(const Dims& d, const void* x, const void* B, const float* dA_cs,
                        const float* dt_T, float* states, hipStream_t s) {
-  const int threads = (int)(64 * (d.N / (16 * NTW)));
-  const size_t lds = (size_t)kJB * (P + kXPad) * 2 + (size_t)kJB * (d.N + kBPad) * 2 +
+  const int64_t cols = 16 * NTW;  // state columns per wave
+  const int64_t npad = (d.N + cols - 1) / cols * cols;
+  const int threads = (int)(64 * (npad / cols));
+  if (threads > 1024) return hipErrorInvalidValue;
+  const size_t lds = (size_t)kJB * (P + kXPad) * 2 + (size_t)kJB * (npad + kBPad) * 2 +
                      (size_t)d.Q * 4;
   auto kern = chunk_state_bf16_kernel<P, NTW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -216,7 +224,7 @@ hipError_t launch_bf16(const Dims& d, const void* x, const void* B, const float*
   if (e != hipSuccess) return e;
   kern<<<(unsigned)(d.B * d.nc * d.H), threads, lds, s>>>(
       (const bf16*)x, (const bf16*)B, dA_cs, dt_T, states, (int)d.L, (int)d.H, (int)d.G,
-      (int)d.N, (int)d.Q, (int)d.nc);
+      (int)d.N, (int)npad, (int)d.Q, (int)d.nc);
   return hipGetLastError();
 }
 
@@ -225,9 +233,15 @@ hipError_t launch_bf16(const Dims& d, const void* x, const void* B, const float*
 hipError_t launch_chunk_state(const Dims& d, const void* x, const void* B, const float* dA_cs,
                               const float* dt_T, float* states, hipStream_t s) {
   if (d.bf16) {
+    // 4 column tiles per wave up to headdim 64, 2 above (accumulators NTW x P/16)
     switch (d.P) {
+      case 16: return launch_bf16<16, 4>(d, x, B, dA_cs, dt_T, states, s);
       case 32: return launch_bf16<32, 4>(d, x, B, dA_cs, dt_T, states, s);
+      case 48: return launch_bf16<48, 4>(d, x, B, dA_cs, dt_T, states, s);
       case 64: return launch_bf16<64, 4>(d, x, B, dA_cs, dt_T, states, s);
+      case 80: return launch_bf16<80, 2>(d, x, B, dA_cs, dt_T, states, s);
+      case 96: return launch_bf16<96, 2>(d, x, B, dA_cs, dt_T, states, s);
+      case 112: return launch_bf16<112, 2>(d, x, B, dA_cs, dt_T, states, s);
       case 128: return launch_bf16<128, 2>(d, x, B, dA_cs, dt_T, states, s);
       default: return hipErrorInvalidValue;
     }

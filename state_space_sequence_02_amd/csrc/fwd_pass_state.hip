@@ -1,6 +1,7 @@
 // fwd_pass_state as one kernel (the pages' own second kernel; the library's
-// default forward runs it as chunk_state + state_passing, which is faster on
-// this chip): the per-chunk B X^T contraction and the
+// default forward runs it over spans of chunks at large sizes and as
+// chunk_state + state_passing below them, both faster on this chip): the
+// per-chunk B X^T contraction and the
 // decayed jump that carries the state across chunks, walking the chunks in
 // order with the running state held in MFMA accumulators (devotd.net news
 // item on the Mamba-2 CUDA Tile forward-pass kernels, section 2: the second

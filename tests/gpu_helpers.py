@@ -28,6 +28,39 @@ def normwise(got, ref):
     return float(err / scale) if scale > 0 else float(err)
 
 
+def headwise(got, ref, head_axis):
+    """The largest normwise error over (batch, head) slices: batch is axis 0,
+    the head axis is given (y [B,L,H,P]: 2; final state [B,H,P,N]: 1; chunk
+    states [B,nc,H,P,N]: 2).  A head whose values are much smaller than the
+    tensor's largest is held to the same relative bar as the rest."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    worst = 0.0
+    for b in range(ref.shape[0]):
+        for h in range(ref.shape[head_axis]):
+            gs = np.take(got[b], h, axis=head_axis - 1)
+            rs = np.take(ref[b], h, axis=head_axis - 1)
+            worst = max(worst, normwise(gs, rs))
+    return worst
+
+
+HEAD_AXIS = {"y": 2, "final_state": 1, "local_states": 2, "start_states": 2}
+
+
+def errors(pairs):
+    """{name: (tensor normwise, worst (batch, head) normwise)} for
+    name -> (got, ref) pairs whose names are keys of HEAD_AXIS."""
+    return {k: (normwise(g, r), headwise(g, r, HEAD_AXIS[k])) for k, (g, r) in pairs.items()}
+
+
+def assert_within(errs, tol):
+    """Every tensor and every (batch, head) slice of it within tol."""
+    for k, (e_all, e_head) in errs.items():
+        assert e_all <= tol, (k, "tensor", e_all, tol)
+        assert e_head <= tol, (k, "worst head", e_head, tol)
+
+
 def f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 

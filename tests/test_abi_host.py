@@ -48,8 +48,15 @@ def _dims(**kw):
     (dict(nheads=6, ngroups=4), m2.MAMBA2_ERR_SHAPE),
     (dict(chunk_size=100), m2.MAMBA2_ERR_UNSUPPORTED),
     (dict(chunk_size=32), m2.MAMBA2_ERR_UNSUPPORTED),          # bf16 needs 64/128/256
-    (dict(headdim=48), m2.MAMBA2_ERR_UNSUPPORTED),
-    (dict(dstate=96), m2.MAMBA2_ERR_UNSUPPORTED),
+    # bfloat16: headdim and dstate any multiple of 16, up to 128 and 512
+    (dict(headdim=48), m2.MAMBA2_OK),
+    (dict(headdim=16, dstate=16), m2.MAMBA2_OK),
+    (dict(headdim=112, dstate=496), m2.MAMBA2_OK),
+    (dict(dstate=96), m2.MAMBA2_OK),
+    (dict(headdim=40), m2.MAMBA2_ERR_UNSUPPORTED),
+    (dict(headdim=144), m2.MAMBA2_ERR_UNSUPPORTED),
+    (dict(dstate=72), m2.MAMBA2_ERR_UNSUPPORTED),
+    (dict(dstate=528), m2.MAMBA2_ERR_UNSUPPORTED),
     (dict(dstate=576), m2.MAMBA2_ERR_UNSUPPORTED),
     (dict(dtype=m2.MAMBA2_DTYPE_F32, chunk_size=48), m2.MAMBA2_ERR_UNSUPPORTED),
     (dict(dtype=m2.MAMBA2_DTYPE_F32, headdim=3, dstate=5, chunk_size=16), m2.MAMBA2_OK),
@@ -193,3 +200,120 @@ def test_fused_state_checks_on_host():
     assert fps(d, wT=None) == m2.MAMBA2_ERR_NULL and "w_T" in m2.mamba2_last_error()
     assert fps(d, hst=ok + 4) == m2.MAMBA2_ERR_ALIGN
     assert fps(d, h0=ok + 8) == m2.MAMBA2_ERR_ALIGN and "init" in m2.mamba2_last_error()
+
+
+def _host_inputs(dtype=None, **kw):
+    """Correctly shaped CPU tensors for a small bfloat16 forward."""
+    import torch
+    d = dict(b=1, L=300, H=4, P=64, N=64, G=2)
+    d.update(kw)
+    io = dtype or torch.bfloat16
+    b, L, H, P, N, G = d["b"], d["L"], d["H"], d["P"], d["N"], d["G"]
+    return {"x": torch.zeros(b, L, H, P, dtype=io), "dt": torch.zeros(b, L, H, dtype=io),
+            "A": torch.zeros(H), "B": torch.zeros(b, L, G, N, dtype=io),
+            "C": torch.zeros(b, L, G, N, dtype=io), "D": torch.zeros(H),
+            "init_state": torch.zeros(b, H, P, N), "y": torch.zeros(b, L, H, P, dtype=io),
+            "final": torch.zeros(b, H, P, N)}
+
+
+def _fwd(t, dims=None, ws=None, **over):
+    import torch
+    a = dict(t)
+    a.update(over)
+    dims = dims or m2.dims_of(t["x"], t["B"], 64)
+    need = m2.mamba2_ssd_workspace_bytes(dims)
+    ws = torch.zeros(need, dtype=torch.uint8) if ws is None else ws
+    m2.mamba2_ssd_forward(dims, a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["init_state"],
+                          a["y"], a["final"], ws, need)
+
+
+@pytest.mark.parametrize("case,status,word", [
+    ("dt_f32_next_to_bf16_x", m2.MAMBA2_ERR_DTYPE, "dt"),
+    ("A_bf16", m2.MAMBA2_ERR_DTYPE, "A"),
+    ("D_bf16", m2.MAMBA2_ERR_DTYPE, "D"),
+    ("init_bf16", m2.MAMBA2_ERR_DTYPE, "init_state"),
+    ("y_f32", m2.MAMBA2_ERR_DTYPE, "y"),
+    ("x_head_slice", m2.MAMBA2_ERR_SHAPE, "x"),
+    ("B_transposed_view", m2.MAMBA2_ERR_SHAPE, "contiguous"),
+    ("C_wrong_groups", m2.MAMBA2_ERR_SHAPE, "C"),
+    ("final_wrong_shape", m2.MAMBA2_ERR_SHAPE, "final_state"),
+    ("all_on_cpu", m2.MAMBA2_ERR_NULL, "GPU"),
+    ("workspace_short", m2.MAMBA2_ERR_WORKSPACE, "workspace"),
+])
+def test_wrapper_rejects_bad_tensors(case, status, word):
+    """The Python wrappers check dtype, shape, contiguity and device of every
+    tensor against dims before calling the C ABI (which sees only pointers)."""
+    import torch
+    t = _host_inputs()
+    over, ws = {}, None
+    if case == "dt_f32_next_to_bf16_x":
+        over["dt"] = t["dt"].float()
+    elif case == "A_bf16":
+        over["A"] = t["A"].bfloat16()
+    elif case == "D_bf16":
+        over["D"] = t["D"].bfloat16()
+    elif case == "init_bf16":
+        over["init_state"] = t["init_state"].bfloat16()
+    elif case == "y_f32":
+        over["y"] = t["y"].float()
+    elif case == "x_head_slice":
+        over["x"] = t["x"][:, :, 1:2]
+    elif case == "B_transposed_view":
+        over["B"] = torch.zeros(1, 300, 64, 2, dtype=torch.bfloat16).transpose(2, 3)
+    elif case == "C_wrong_groups":
+        over["C"] = torch.zeros(1, 300, 1, 64, dtype=torch.bfloat16)
+    elif case == "final_wrong_shape":
+        over["final"] = torch.zeros(1, 4, 64, 32)
+    elif case == "workspace_short":
+        ws = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(m2.Mamba2Error) as ei:
+        _fwd(t, ws=ws, **over)
+    assert ei.value.status == status
+    assert word in str(ei.value)
+
+
+def test_wrapper_checks_every_entry_point():
+    """Stage, decode and backward wrappers reject a wrongly typed tensor too."""
+    import torch
+    t = _host_inputs()
+    dims = m2.dims_of(t["x"], t["B"], 64)
+    cs = torch.zeros(1, 4, 5, 64)
+    with pytest.raises(m2.Mamba2Error) as ei:
+        m2.mamba2_chunk_cumsum(dims, t["dt"].float(), t["A"], cs, cs)
+    assert ei.value.status == m2.MAMBA2_ERR_DTYPE
+    with pytest.raises(m2.Mamba2Error) as ei:
+        m2.mamba2_chunk_cumsum(dims, t["dt"], t["A"], cs[:, :, :4], cs)
+    assert ei.value.status == m2.MAMBA2_ERR_SHAPE and "dA_cs" in str(ei.value)
+    st = torch.zeros(1, 5, 4, 64, 64)
+    with pytest.raises(m2.Mamba2Error) as ei:
+        m2.mamba2_chunk_state(dims, t["x"], t["B"], cs, cs, st.transpose(3, 4))
+    assert ei.value.status == m2.MAMBA2_ERR_SHAPE and "contiguous" in str(ei.value)
+    with pytest.raises(m2.Mamba2Error) as ei:
+        m2.mamba2_state_passing(dims, st, cs, t["init_state"].double(), None)
+    assert ei.value.status == m2.MAMBA2_ERR_DTYPE
+    with pytest.raises(m2.Mamba2Error) as ei:
+        m2.mamba2_chunk_scan(dims, t["x"], t["B"], t["C"], cs, cs, st, t["D"], t["y"][:, :299])
+    assert ei.value.status == m2.MAMBA2_ERR_SHAPE and "y" in str(ei.value)
+    d1 = m2.make_dims(1, 1, 4, 64, 64, 2, 64, torch.bfloat16)
+    x1 = torch.zeros(1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(m2.Mamba2Error) as ei:
+        m2.mamba2_decode_step(d1, x1, torch.zeros(1, 4, dtype=torch.bfloat16), t["A"],
+                              torch.zeros(1, 2, 64, dtype=torch.bfloat16),
+                              torch.zeros(1, 2, 64, dtype=torch.bfloat16), None,
+                              torch.zeros(1, 4, 64, 64, dtype=torch.bfloat16), x1)
+    assert ei.value.status == m2.MAMBA2_ERR_DTYPE and "state" in str(ei.value)
+    g = {k: torch.zeros_like(v) for k, v in t.items()}
+    with pytest.raises(m2.Mamba2Error) as ei:
+        m2.mamba2_ssd_backward(dims, t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], None,
+                               t["y"], None, g["x"], g["dt"].float(), g["A"], g["B"], g["C"],
+                               g["D"], None, torch.zeros(16, dtype=torch.uint8), 16)
+    assert ei.value.status == m2.MAMBA2_ERR_DTYPE and "ddt" in str(ei.value)
+    # a correctly typed call on host tensors is refused for the device, not the types
+    with pytest.raises(m2.Mamba2Error) as ei:
+        m2.ssd_forward(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["init_state"],
+                       chunk_size=64)
+    assert ei.value.status == m2.MAMBA2_ERR_NULL and "GPU" in str(ei.value)
+    with pytest.raises(m2.Mamba2Error) as ei:
+        m2.ssd_forward(t["x"], t["dt"].float(), t["A"], t["B"], t["C"], t["D"], None,
+                       chunk_size=64)
+    assert ei.value.status == m2.MAMBA2_ERR_DTYPE

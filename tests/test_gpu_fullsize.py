@@ -1,8 +1,9 @@
 """Parity at the two long workloads (L = 65536, N = 256 and L = 262144,
 N = 512, G = 4), in the launch configuration the benchmark times
 (mamba2_ssd_forward).  The oracle recomputes whole heads (every token, every
-headdim row) for a sample of heads drawn from different B/C groups, plus the
-chunk-start states of those heads through the stage entry points."""
+headdim row) for a sample of heads that covers every B/C group (at G = 4: heads
+0, 9, 17, 25, 31 of groups 0, 1, 2, 3, 3), plus the chunk-start states of those
+heads through the stage entry points."""
 import numpy as np
 import pytest
 import torch
@@ -45,7 +46,9 @@ def test_full_size_forward_sampled_heads(m2, name):
     m2.mamba2_state_passing(dims, st, cs, g["init_state"], None)
     torch.cuda.synchronize()
     H, G = w.nheads, w.ngroups
-    heads = sorted({0, H // 2 + 1, H - 1})
+    HG = H // G
+    heads = sorted({0, H // 2 + 1, H - 1} | {g * HG + 1 for g in range(1, G)})
+    assert {h // HG for h in heads} == set(range(G))
     for h in heads:
         o = _head_slice(inp, h, G, H)
         oy, ofin, ohs = oracle.ssd_recurrence(o["x"], o["dt"], o["A"], o["B"], o["C"], o["D"],

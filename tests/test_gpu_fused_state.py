@@ -18,7 +18,8 @@ import torch
 
 import oracle
 import ssd_inputs
-from gpu_helpers import TOL, f32, f64, normwise, oracle_inputs, run_forward, say, to_gpu
+from gpu_helpers import (TOL, assert_within, errors, f32, f64, normwise, oracle_inputs,
+                         run_forward, say, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,10 +93,9 @@ def test_fwd_pass_state_isolated(m2, w):
     _, ofin, ohs = oracle.ssd_recurrence(o["x"], o["dt"], o["A"], o["B"], o["C"], o["D"],
                                          o["init_state"], chunk_size=w.chunk_size,
                                          want_hstart=True)
-    eh, ef = normwise(f64(hst), ohs), normwise(f64(fin), ofin)
-    say(f"  start_states {eh:.3e} final {ef:.3e}")
-    assert eh <= BT
-    assert ef <= BT
+    errs = errors({"start_states": (f64(hst), ohs), "final_state": (f64(fin), ofin)})
+    say(f"  errors (tensor, worst head) {errs}")
+    assert_within(errs, BT)
 
 
 @pytest.mark.parametrize("w", SHAPES, ids=lambda w: w.name)
@@ -115,10 +115,9 @@ def test_forward_fused_matches_oracle(m2, w):
     torch.cuda.synchronize()
     oy, ofin, _ = oracle.ssd_recurrence(o["x"], o["dt"], o["A"], o["B"], o["C"], o["D"],
                                         o["init_state"], chunk_size=w.chunk_size)
-    ey, ef = normwise(f64(y), oy), normwise(f64(fin), ofin)
-    say(f"  y {ey:.3e} final {ef:.3e}")
-    assert ey <= BT
-    assert ef <= BT
+    errs = errors({"y": (f64(y), oy), "final_state": (f64(fin), ofin)})
+    say(f"  errors (tensor, worst head) {errs}")
+    assert_within(errs, BT)
     # and with the default state path (chunk_state + state_passing)
     y2, fin2 = run_forward(m2, g, w.chunk_size)
     assert normwise(f64(y), f64(y2)) <= BT

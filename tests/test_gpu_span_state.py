@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import ssd_inputs
-from gpu_helpers import TOL, f64, normwise, oracle_inputs, run_forward, say, to_gpu
+from gpu_helpers import TOL, assert_within, errors, f64, oracle_inputs, run_forward, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -107,10 +107,9 @@ def test_span_forward_matches_oracle(m2, w):
     y, fin = run_forward(m2, g, w.chunk_size)
     oy, ofin, _ = oracle.ssd_recurrence(o["x"], o["dt"], o["A"], o["B"], o["C"], o["D"],
                                         o["init_state"], chunk_size=w.chunk_size)
-    ey, ef = normwise(f64(y), oy), normwise(f64(fin), ofin)
-    say(f"  y {ey:.3e} final {ef:.3e}")
-    assert ey <= BT
-    assert ef <= BT
+    errs = errors({"y": (f64(y), oy), "final_state": (f64(fin), ofin)})
+    say(f"  errors (tensor, worst head) {errs}")
+    assert_within(errs, BT)
 
 
 def test_span_forward_is_deterministic(m2):
