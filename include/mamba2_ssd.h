@@ -175,6 +175,31 @@ int mamba2_ssd_forward(const mamba2_dims* dims, const void* x, const void* dt,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mamba2_ssd_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, with the workspace taken from a static
+ * device array of MAMBA2_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends.  The caller passes inputs and
+ * outputs only; the call allocates and frees nothing.  Sizes whose
+ * mamba2_ssd_workspace_bytes exceed the array are rejected with
+ * MAMBA2_ERR_WORKSPACE before any launch.  The array's address on the
+ * current device is looked up once per device (hipGetSymbolAddress) and
+ * kept; the current device must be the one the pointers and the stream
+ * belong to.  Every call on one GPU shares that GPU's array and it keeps the
+ * last call's contents (no part needs clearing: each piece is written
+ * before it is read within a call), so calls that overlap on one GPU - on
+ * different streams, or from different threads - race and give wrong
+ * results: order them on one stream or otherwise.  Other rules as for
+ * mamba2_ssd_forward.
+ */
+#define MAMBA2_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+int mamba2_ssd_forward_noalloc(const mamba2_dims* dims, const void* x, const void* dt,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const float* init_state, void* y, float* final_state,
+                               void* stream);
+
+/*
  * Same as mamba2_ssd_forward, then waits for the work to finish and writes
  * the device time of each stage in milliseconds to stage_ms[0..3]
  * (chunk_cumsum, chunk_state, state_passing, chunk_scan; on the span path

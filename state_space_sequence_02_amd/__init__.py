@@ -50,8 +50,11 @@ EXPORTS = (
     "mamba2_ssd_forward_profile", "mamba2_fwd_pass_state", "mamba2_ssd_forward_fused",
     "mamba2_decode_step", "mamba2_ssd_backward_workspace_bytes",
     "mamba2_ssd_backward", "mamba2_ssd_backward_profile", "mamba2_status_string",
-    "mamba2_last_error",
+    "mamba2_last_error", "mamba2_ssd_forward_noalloc",
 )
+
+# bytes of the static per-GPU scratch behind mamba2_ssd_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class Mamba2Dims(ctypes.Structure):
@@ -91,6 +94,7 @@ def _load():
         "mamba2_ssd_forward": ([D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P], ctypes.c_int),
         "mamba2_ssd_forward_profile": ([D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
                                         ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
+        "mamba2_ssd_forward_noalloc": ([D, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "mamba2_decode_step": ([D, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "mamba2_fwd_pass_state": ([D, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "mamba2_ssd_forward_fused": ([D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P],
@@ -308,6 +312,23 @@ def mamba2_ssd_forward(dims, x, dt, A, B, C, D, init_state, y, final_state, work
                                    _ptr(C), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
                                    _ptr(workspace), int(workspace_bytes), _stream(stream)),
            "mamba2_ssd_forward")
+
+
+def mamba2_ssd_forward_noalloc(dims, x, dt, A, B, C, D, init_state, y, final_state,
+                               stream=None):
+    """mamba2_ssd_forward with the library's static per-GPU scratch as the
+    workspace (no allocation; calls that overlap on one GPU race)."""
+    w = "mamba2_ssd_forward_noalloc"
+    for role, name, t in (("x", "x", x), ("dt", "dt", dt), ("A", "A", A), ("B", "B", B),
+                          ("C", "C", C), ("y", "y", y)):
+        _req(w, dims, role, name, t)
+    _req(w, dims, "D", "D", D, optional=True)
+    _req(w, dims, "state", "init_state", init_state, optional=True)
+    _req(w, dims, "state", "final_state", final_state, optional=True)
+    _same_device(w, x, dt, A, B, C, D, init_state, y, final_state)
+    _check(_lib.mamba2_ssd_forward_noalloc(ctypes.byref(dims), _ptr(x), _ptr(dt), _ptr(A),
+                                           _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), _ptr(y),
+                                           _ptr(final_state), _stream(stream)), w)
 
 
 def mamba2_ssd_forward_profile(dims, x, dt, A, B, C, D, init_state, y, final_state, workspace,

@@ -6,8 +6,15 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "launch.h"
 #include "mamba2_ssd.h"
+
+// Workspace of mamba2_ssd_forward_noalloc: one copy per GPU, held for the
+// process's lifetime.  Host code never uses this name as an address (it is a
+// host-side stand-in there); it uses the device address looked up below.
+static __device__ __align__(256) unsigned char scratch[MAMBA2_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -215,6 +222,32 @@ int check_forward_args(const mamba2_dims* dims, m2::Dims* d, const void* x, cons
   if (workspace_bytes < w.total)
     return fail(MAMBA2_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
                 w.total);
+  return MAMBA2_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MAMBA2_ERR_HIP, "device %d is beyond the %d devices the scratch table covers", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p & 255u) != 0)
+      return fail(MAMBA2_ERR_HIP, "scratch has no 256-byte aligned device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return MAMBA2_OK;
 }
 
@@ -534,6 +567,25 @@ int mamba2_ssd_forward(const mamba2_dims* dims, const void* x, const void* dt, c
   CHECK(check_forward_args(dims, &d, x, dt, A, B, C, D, init_state, y, final_state, workspace,
                            workspace_bytes));
   return enqueue_forward(d, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                         (hipStream_t)stream, nullptr);
+}
+
+int mamba2_ssd_forward_noalloc(const mamba2_dims* dims, const void* x, const void* dt,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const float* init_state, void* y, float* final_state,
+                               void* stream) {
+  m2::Dims d;
+  CHECK(validate(dims, &d));
+  const size_t need_bytes = plan(d).total;
+  if (need_bytes > MAMBA2_NOALLOC_SCRATCH_BYTES)
+    return fail(MAMBA2_ERR_WORKSPACE,
+                "these sizes need %zu bytes of workspace; the static scratch holds %zu",
+                need_bytes, (size_t)MAMBA2_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  CHECK(scratch_on_current_device(&ws));
+  CHECK(check_forward_args(dims, &d, x, dt, A, B, C, D, init_state, y, final_state, ws,
+                           MAMBA2_NOALLOC_SCRATCH_BYTES));
+  return enqueue_forward(d, x, dt, A, B, C, D, init_state, y, final_state, ws,
                          (hipStream_t)stream, nullptr);
 }
 

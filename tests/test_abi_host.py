@@ -317,3 +317,21 @@ def test_wrapper_checks_every_entry_point():
         m2.ssd_forward(t["x"], t["dt"].float(), t["A"], t["B"], t["C"], t["D"], None,
                        chunk_size=64)
     assert ei.value.status == m2.MAMBA2_ERR_DTYPE
+
+
+def test_noalloc_rejects_oversize_on_host():
+    """mamba2_ssd_forward_noalloc refuses sizes whose workspace exceeds its
+    static scratch before any device call (checked without a GPU)."""
+    big = _dims(seqlen=65536, nheads=32, dstate=256)
+    assert m2.mamba2_ssd_workspace_bytes(big) > m2.NOALLOC_SCRATCH_BYTES
+    ok = 1 << 20
+    rc = m2._lib.mamba2_ssd_forward_noalloc(ctypes.byref(big), ok, ok, ok, ok, ok, None, None, ok,
+                                            None, None)
+    assert rc == m2.MAMBA2_ERR_WORKSPACE and "scratch" in m2.mamba2_last_error()
+    bad = _dims(headdim=40)
+    rc = m2._lib.mamba2_ssd_forward_noalloc(ctypes.byref(bad), ok, ok, ok, ok, ok, None, None, ok,
+                                            None, None)
+    assert rc == m2.MAMBA2_ERR_UNSUPPORTED
+    text = open(HEADER).read()
+    assert "#define MAMBA2_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in text
+    assert m2.NOALLOC_SCRATCH_BYTES == 128 << 20
