@@ -59,9 +59,28 @@ def span_plan(w, cus=256):
     return None
 
 
+def scan_plan(w, cus=256):
+    """Heads per workgroup of span_scan (the span replay fused with the output
+    stage), or None where the forward runs the replay and the grouped
+    chunk_scan instead (same rule as the library: state size 64 or 128 on the
+    span path; 4 heads where the grid still gives every CU a workgroup, else 2;
+    an even number of heads per group)."""
+    plan = span_plan(w, cus)
+    if not plan or w.dstate not in (64, 128):
+        return None
+    K = plan[0]
+    hg = w.nheads // w.ngroups
+    ng = -(-w.nchunks // K)
+    if hg % 4 == 0 and w.batch * ng * w.nheads // 4 >= cus:
+        return 4
+    return 2 if hg % 2 == 0 else None
+
+
 def forward_stages(w, cus=256):
     """Names of the four timed slots of mamba2_ssd_forward_profile."""
     if span_plan(w, cus):
+        if scan_plan(w, cus):
+            return ("chunk_cumsum", "span_end", "span_jump", "span_scan")
         return ("chunk_cumsum", "span_end", "span_pass", "chunk_scan")
     return STAGES
 
@@ -104,6 +123,17 @@ def stage_model(w, cus=256):
         m["span_pass"] = dict(
             flops=2 * ss // 4 + 2 * N * P * tok * H * frac,
             bytes=(ss + dec + init + ss + fin) + (x * frac + bc * frac + 2 * csb + ss + hs))
+        # fused path: the jump alone, then span_scan (replay and output in one
+        # pass over blocks of 32 steps: x, B, C, sums and the span start
+        # states read once, y written once; C B^T of each block once per group)
+        m["span_jump"] = dict(flops=2 * ss // 4, bytes=ss + dec + init + ss + fin)
+        rb = 32
+        nblk = nc * (Q // rb)
+        ufrac = (nblk - ng) / nblk                    # blocks whose state update runs
+        m["span_scan"] = dict(
+            flops=tok * H * (2 * N * P + 2 * N * P * ufrac + (rb + 1) * P + 2 * P)
+            + tok * G * (rb + 1) * N,
+            bytes=x + 2 * bc + 2 * csb + ss + H * 4 + x)
     return m
 
 
@@ -276,6 +306,9 @@ def effective_flops(w, stage):
     tok = B * L
     if stage == "chunk_scan":
         return tok * H * (2 * N * P + (Q + 1) * (N + P) + 2 * P)
+    if stage == "span_scan":
+        m = stage_model(w)["span_scan"]
+        return m["flops"] - tok * w.ngroups * 33 * N + tok * H * 33 * N
     return stage_model(w)[stage]["flops"]
 
 
@@ -410,6 +443,8 @@ KERNEL_SOURCES = {
     "state_passing": ("state_passing.hip", "common.h"),
     "span_end": ("state_span.hip", "common.h"),
     "span_pass": ("state_span.hip", "common.h"),
+    "span_jump": ("state_span.hip", "common.h"),
+    "span_scan": ("span_scan.hip", "common.h"),
     "chunk_scan": ("chunk_scan_grouped.hip", "common.h"),
     "adjoint_state": ("chunk_state_grouped.hip", "common.h"),
     "reverse_pass": ("state_passing.hip", "common.h"),
@@ -525,7 +560,9 @@ def sweep_bench(args):
             byt = sum(model[s]["bytes"] for s in names)
             flo = sum(model[s]["flops"] for s in names)
             plan = span_plan(w, cus)
-            path = (f"span K={plan[0]} R={plan[1]}" if plan else
+            sp = scan_plan(w, cus)
+            path = (f"span K={plan[0]} R={plan[1]}" + (f", span_scan R={sp}" if sp else "")
+                    if plan else
                     ("split, bf16 start states" if grouped_path(w) else "split, per head"))
             print(json.dumps({
                 "workload": w.name, "seqlen": L, "dstate": N, "nheads": w.nheads,

@@ -161,13 +161,17 @@ int enqueue_forward(const m2::Dims& d, const void* x, const void* dt, const floa
     // jump across spans and the replay that writes the chunk-start states
     // (stage slot 2)
     float* span_decay = (float*)((char*)states + span_bytes);
+    // the replay fused with the output stage where span_scan covers the
+    // sizes (stage slots: span-end states, jump across spans, span_scan)
+    const int Rs = m2::span_scan_heads(d, K);
     if (e == hipSuccess)
       e = m2::launch_fwd_pass_state_span(d, K, x, B, dA_cs, dt_T, init_state, states, span_decay,
-                                         hst, final_state, s, ev ? ev[2] : nullptr);
+                                         hst, final_state, s, ev ? ev[2] : nullptr, Rs == 0);
     if (e != hipSuccess) return hip_status(e, "fwd_pass_state launch");
     if (ev) e = hipEventRecord(ev[3], s);
     if (e == hipSuccess)
-      e = m2::launch_chunk_scan_grouped(d, x, B, C, dA_cs, dt_T, hst, D, y, part, s);
+      e = Rs ? m2::launch_span_scan(d, K, Rs, x, B, C, dA_cs, dt_T, states, D, y, s)
+             : m2::launch_chunk_scan_grouped(d, x, B, C, dA_cs, dt_T, hst, D, y, part, s);
     if (e != hipSuccess) return hip_status(e, "chunk_scan launch");
     if (ev) e = hipEventRecord(ev[4], s);
     return hip_status(e, "event record");

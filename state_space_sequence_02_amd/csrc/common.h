@@ -81,6 +81,26 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Waits until at most n of this wave's vector memory operations are
+// outstanding (and its LDS operations are done).  n is wave-uniform.  Vector
+// memory operations retire in issue order, so with n = the number of
+// operations issued after a given load, that load has landed.
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define M2_W(k) \
+  case k: __builtin_amdgcn_s_waitcnt(0x0070 | ((k) & 15) | (((k) >> 4) << 14)); break;
+    M2_W(0) M2_W(1) M2_W(2) M2_W(3) M2_W(4) M2_W(5) M2_W(6) M2_W(7) M2_W(8) M2_W(9)
+    M2_W(10) M2_W(11) M2_W(12) M2_W(13) M2_W(14) M2_W(15) M2_W(16) M2_W(17) M2_W(18)
+    M2_W(19) M2_W(20) M2_W(21) M2_W(22) M2_W(23) M2_W(24) M2_W(25) M2_W(26) M2_W(27)
+    M2_W(28) M2_W(29) M2_W(30) M2_W(31) M2_W(32) M2_W(33) M2_W(34) M2_W(35) M2_W(36)
+    M2_W(37) M2_W(38) M2_W(39) M2_W(40) M2_W(41) M2_W(42) M2_W(43) M2_W(44) M2_W(45)
+    M2_W(46) M2_W(47) M2_W(48) M2_W(49) M2_W(50) M2_W(51) M2_W(52) M2_W(53) M2_W(54)
+    M2_W(55) M2_W(56) M2_W(57) M2_W(58) M2_W(59) M2_W(60) M2_W(61) M2_W(62)
+#undef M2_W
+    default: __builtin_amdgcn_s_waitcnt(0x0070); break;  // vmcnt(0)
+  }
+}
+
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }

@@ -78,10 +78,22 @@ hipError_t launch_bwd_param_sums(const Dims& d, const float* dA_part, const floa
 // (may be null) is recorded after the span-end kernel.
 int span_chunks(const Dims& d);
 size_t span_states_bytes(const Dims& d, int K);
+// replay = false stops after the jump across spans (span_states then hold
+// every span's start state, for span_scan).
 hipError_t launch_fwd_pass_state_span(const Dims& d, int K, const void* x, const void* B,
                                       const float* dA_cs, const float* dt_T, const float* init,
                                       float* span_states, float* span_decay, void* hst,
-                                      float* final_state, hipStream_t s, hipEvent_t mid);
+                                      float* final_state, hipStream_t s, hipEvent_t mid,
+                                      bool replay);
+
+// span_scan (span_scan.hip): the replay of each span fused with compute_out,
+// from the span start states the jump leaves in span_states; y only.
+// span_scan_heads gives the heads per workgroup (0 = not covered: the replay
+// and the grouped chunk_scan run instead).
+int span_scan_heads(const Dims& d, int K);
+hipError_t launch_span_scan(const Dims& d, int K, int R, const void* x, const void* B,
+                            const void* C, const float* dA_cs, const float* dt_T,
+                            const float* span_states, const float* D, void* y, hipStream_t s);
 
 bool fused_state_supported(const Dims& d);
 hipError_t launch_chunk_weights(const Dims& d, const float* dA_cs, const float* dt_T, float* w_T,

@@ -324,7 +324,7 @@ def _zero_dt_tokens(L, Q):
 
 # Shapes whose forward takes each kind of kernel: per-head bfloat16 (headdim
 # 32), the split form with the grouped output stage, the span path (heads
-# sharing B, and state size 512 over column halves), and float32.
+# sharing B, and state size 512 over column halves), span_scan, and float32.
 DT_ZERO = [
     _custom(name="dt0_P32_split", batch=1, seqlen=1000, nheads=3, headdim=32, dstate=64,
             ngroups=1, chunk_size=64, init_state=True, seed=61),
@@ -334,6 +334,9 @@ DT_ZERO = [
             ngroups=1, chunk_size=64, init_state=True, seed=63),
     _custom(name="dt0_span_N512", batch=4, seqlen=4096 - 19, nheads=32, headdim=64, dstate=512,
             ngroups=4, chunk_size=64, seed=64),
+    # span_scan (the span replay fused with the output stage)
+    _custom(name="dt0_span_scan_N128", batch=2, seqlen=8192 - 45, nheads=32, headdim=64,
+            dstate=128, ngroups=2, chunk_size=64, init_state=True, seed=60),
     _custom(name="dt0_f32", batch=1, seqlen=700, nheads=2, headdim=16, dstate=16, ngroups=1,
             chunk_size=64, dtype="f32", init_state=True, seed=65),
 ]
@@ -375,6 +378,8 @@ MEMORYLESS = [
             ngroups=2, chunk_size=64, init_state=True, seed=66),
     _custom(name="memoryless_Q256_span", batch=1, seqlen=8192, nheads=64, headdim=64, dstate=256,
             ngroups=1, chunk_size=256, init_state=True, seed=67),
+    _custom(name="memoryless_span_scan_N64", batch=1, seqlen=4096 - 5, nheads=64, headdim=64,
+            dstate=64, ngroups=2, chunk_size=128, init_state=True, seed=70),
     _custom(name="memoryless_Q64_f32", batch=1, seqlen=300, nheads=2, headdim=16, dstate=16,
             ngroups=1, chunk_size=64, dtype="f32", init_state=True, seed=68),
 ]

@@ -3,8 +3,10 @@
 For bfloat16 with headdim 64, state size 64, 128 or 256 and enough
 (batch, head, span) work to give every CU a workgroup, mamba2_ssd_forward
 runs fwd_pass_state over spans of K = 8 (else 4) chunks: span-end states,
-the jump across spans, and a replay of every span that writes the chunk-start
-states, with 1, 2 or 4 heads of a group per workgroup.  These shapes meet
+the jump across spans, and then either a replay of every span that writes the
+chunk-start states for the grouped chunk_scan (state size 256 and 512), or
+span_scan, the replay fused with the output stage (state size 64 and 128),
+with 1, 2 or 4 heads of a group per workgroup.  These shapes meet
 that rule (checked below with the device's CU count) and cover every (chunk
 size, state size) pair, 1, 2 and 4 heads per workgroup, ragged last chunks, a
 last span of one chunk, several groups and batches, with and without the
@@ -54,6 +56,10 @@ SHAPES = [
     _w("span_Q256_N512_G3_K4", 3000, 96, 512, 3, 256, init=False, seed=104),
     # N = 256, one head per workgroup, two workgroups per CU (three-buffer ring)
     _w("span_Q64_N256_G2_R1_two_per_cu", 4096 - 3, 66, 256, 2, 64, seed=105),
+    # span_scan with four heads per workgroup at the chunk sizes not covered above
+    _w("span_scan_Q64_N128_R4_ragged", 8192 - 45, 32, 128, 2, 64, Bn=2, seed=106),
+    _w("span_scan_Q256_N64_R4", 16384 - 7, 64, 64, 4, 256, Bn=2, init=False, seed=107),
+    _w("span_scan_Q128_N64_G2", 4096 + 100, 32, 64, 2, 128, Bn=2, seed=108),
 ]
 
 # (span length, heads per workgroup) each shape reaches on a 256-CU device
@@ -92,12 +98,41 @@ def span_heads(w, K, cus):
     return 1
 
 
+def scan_heads(w, K, cus):
+    """Heads per workgroup of span_scan, the span replay fused with the output
+    stage (0: the replay and the grouped chunk_scan run instead): state size
+    64 or 128; 4 heads where the grid still gives every CU a workgroup, else
+    2; an even number of heads per group."""
+    if not K or w.dstate not in (64, 128):
+        return 0
+    hg = w.nheads // w.ngroups
+    ng = -(-(-(-w.seqlen // w.chunk_size)) // K)
+    if hg % 4 == 0 and w.batch * ng * w.nheads // 4 >= cus:
+        return 4
+    return 2 if hg % 2 == 0 else 0
+
+
+def test_span_scan_cases_cover_every_variant():
+    """The shapes above reach span_scan with 2 and 4 heads per workgroup at
+    state sizes 64 and 128, over every chunk size (on a 256-CU device)."""
+    seen = set()
+    for w in SHAPES:
+        K = span_chunks(w, 256)
+        r = scan_heads(w, K, 256)
+        if r:
+            seen.add((w.dstate, r, w.chunk_size))
+    for n in (64, 128):
+        for r in (2, 4):
+            assert any((n, r, q) in seen for q in (64, 128, 256)), (n, r)
+        assert {q for (nn, _, q) in seen if nn == n} == {64, 128, 256}, n
+
+
 @pytest.mark.parametrize("w", SHAPES, ids=lambda w: w.name)
 def test_span_forward_matches_oracle(m2, w):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     K = span_chunks(w, cus)
     R = span_heads(w, K, cus) if K else 0
-    say(f"[span] {w} K={K} R={R}")
+    say(f"[span] {w} K={K} R={R} span_scan R={scan_heads(w, K, cus)}")
     assert K > 0, "shape does not reach the span path on this device"
     if cus == 256 and w.name in EXPECT:
         assert (K, R) == EXPECT[w.name]
