@@ -91,21 +91,41 @@ struct SpanCfg {
   static_assert(Q % RB == 0 && BPC >= 2, "chunk size");
 };
 
-// 16-byte chunk positions inside LDS rows (involutions).  x rows hold 8
-// chunks; B rows N/8.  A transpose read of B touches rows 8 g + q + {0, 4}
-// (g, q = 0..3) at 4 consecutive chunks of one half: (q << 2) moves the four
-// q rows onto different 64-byte groups of a bank period.
+// 16-byte chunk positions inside LDS rows (involutions).  The LDS has 64
+// banks of 4 bytes and serves an 8-byte (transposed) read 32 lanes at a
+// time, so those 32 lanes must address 32 distinct 8-byte bank slots.  x rows
+// hold 8 chunks: a transposed read of x touches rows 8 g + d (+ 4), d =
+// 0..3, g = 0, 1, at two chunks, both halves; (r & 7) places them on 32
+// distinct slots.  B rows hold N/8 chunks: a transposed read of B touches the
+// same rows at one pair of chunks (both halves of each); the pair moves by an
+// even amount distinct for each of those 8 rows (2 (r % 4) + 8 ((r / 8) % 2)),
+// or, with 8 chunks per row (N = 64, where odd and even rows already fall on
+// different halves of the bank period), by 2 ((r / 2) % 2) + 4 ((r / 8) % 2).
 __device__ __forceinline__ int sx(int r, int c) { return c ^ (r & 7); }
-template <int N>
+// That needs each B tile to hold 16 consecutive state columns (ALT), which
+// leaves a lane's accumulators of the two tiles 16 columns apart, so the
+// replay, which stores a bfloat16 state at every chunk start, keeps tiles of
+// interleaved columns instead (8 contiguous columns per lane, one 16-byte
+// store) at the price of 2-way conflicted B reads: all lanes read the same
+// half of their chunks, and (4 (r % 4)) spreads the rows over 16 chunks.
+template <int N, bool ALT>
 __device__ __forceinline__ int sb(int r, int c) {
-  return c ^ (((r & 3) << 2) & (N / 8 - 1));
+  if constexpr (!ALT) return c ^ (((r & 3) << 2) & (N / 8 - 1));
+  if constexpr (N == 64) return c ^ (2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1));
+  return c ^ ((2 * (r & 3) + 8 * ((r >> 3) & 1)) & (N / 8 - 1));
+}
+// Column of accumulator (nt, e) of lane group grp within a wave's 32-column
+// group: ALT tiles 16 nt + 4 grp + e, else 8 grp + 4 nt + e.
+template <bool ALT>
+__device__ __forceinline__ int acc_col(int nt, int grp) {
+  return ALT ? 16 * nt + 4 * grp : 8 * grp + 4 * nt;
 }
 
 // Direct-to-LDS loads of block `blk` (time steps tok0 .. tok0 + 31 of chunk
 // c) into buffer `buf` (an LDS byte address): load k of the block goes to
 // wave k % NW.  Rows past L are clamped to L - 1: their weight is 0 (dt is
 // zero-padded).
-template <int Q, int N, int R, int LDN>
+template <int Q, int N, int R, int LDN, bool ALT>
 __device__ __forceinline__ void issue_block(uint32_t buf, const bf16* __restrict__ x,
                                             const bf16* __restrict__ Bm,
                                             const float* __restrict__ dA_cs,
@@ -130,7 +150,7 @@ __device__ __forceinline__ void issue_block(uint32_t buf, const bf16* __restrict
       const int row = s / (N / 8), pos = s % (N / 8);
       int64_t t = tok0 + row;
       if (t > L - 1) t = L - 1;
-      dma16(Bm + (((int64_t)b * L + t) * G + g) * LDN + ncol0 + 8 * sb<N>(row, pos),
+      dma16(Bm + (((int64_t)b * L + t) * G + g) * LDN + ncol0 + 8 * sb<N, ALT>(row, pos),
             buf + C::XS + s * 16);
     } else if (k == C::XT + C::BT) {  // cumulative sums and dt of the R heads
       const int r = lane >> 4, q = lane & 15;
@@ -153,7 +173,7 @@ __device__ __forceinline__ void issue_block(uint32_t buf, const bf16* __restrict
 // (lanes past the heads load a valid duplicate into unused LDS), so issuing
 // a block takes no lane masks or branches on the kind.  Valid while the
 // block lies inside the sequence (no clamping needed).
-template <int Q, int N, int R, int LDN>
+template <int Q, int N, int R, int LDN, bool ALT>
 struct DmaPlan {
   using C = SpanCfg<Q, N, R>;
   static constexpr int NJ = (C::TOT + C::NW - 1) / C::NW;
@@ -187,7 +207,7 @@ struct DmaPlan {
         const int s = (k - C::XT) * 64 + lane;
         const int row = s / (N / 8), pos = s % (N / 8);
         p[j] = (const char*)(Bm + (((int64_t)b * L + tok0 + row) * G + g) * LDN + ncol0 +
-                             8 * sb<N>(row, pos));
+                             8 * sb<N, ALT>(row, pos));
         dst[j] = C::XS + (k - C::XT) * 1024;
         st[j] = (int64_t)C::RB * G * LDN * 2;
       } else if (k == C::XT + C::BT) {
@@ -238,7 +258,7 @@ __device__ __forceinline__ void store_hst(bf16* __restrict__ hst, const f32x4 (&
 #pragma unroll
   for (int m = 0; m < R; ++m) {
     const int r = tile_head<C::NW, R>(w, m);
-    const int ncol = 32 * tile_cols<C::NW, R>(w, m) + 8 * grp;
+    const int ncol = 32 * tile_cols<C::NW, R>(w, m) + 8 * grp;  // interleaved tiles
     bf16* dst = hst + ((((int64_t)b * nc + c) * H + h0 + r) * 64 + L16) * LDN + ncol0 + ncol;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
@@ -292,18 +312,20 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
   const int nw = C::TOT / C::NW + (w < C::TOT % C::NW ? 1 : 0);
 
   // acc[m][nt][pt][e] = state of head h0 + tile_head(w, m) at
-  // [p = 16 pt + L16][n = 32 tile_cols(w, m) + 8 grp + 4 nt + e]
+  // [p = 16 pt + L16][n = 32 tile_cols(w, m) + acc_col(nt, grp) + e]
+  constexpr bool ALT = !REPLAY;
   f32x4 acc[R][2][4];
 #pragma unroll
   for (int m = 0; m < R; ++m) {
     const int r = tile_head<C::NW, R>(w, m);
-    const int ncol = 32 * tile_cols<C::NW, R>(w, m) + 8 * grp;
+    const int ncol = 32 * tile_cols<C::NW, R>(w, m);
     const float* sst = span_states + (((int64_t)b * ng + s) * H + h0 + r) * 64 * LDN + ncol0;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        acc[m][nt][pt] = REPLAY ? *(const f32x4*)(sst + (16 * pt + L16) * LDN + ncol + 4 * nt)
+        acc[m][nt][pt] = REPLAY ? *(const f32x4*)(sst + (16 * pt + L16) * LDN + ncol +
+                                                  acc_col<ALT>(nt, grp))
                                 : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float dsum[R];
@@ -312,7 +334,7 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
 
   const uint32_t sbase = lds_addr(smem);
   __builtin_amdgcn_s_waitcnt(0);  // the start states are in registers
-  DmaPlan<Q, N, R, LDN> plan;
+  DmaPlan<Q, N, R, LDN, ALT> plan;
   plan.init(x, Bm, dA_cs, dt_T, c0, b, h0, g, L, H, G, nc, ncol0);
   // blocks from `nfast` on reach past the sequence end: their rows are clamped
   const int nfast = min(nblk, (int)(((int64_t)L - (int64_t)c0 * Q) / C::RB));
@@ -321,7 +343,7 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
     if (j < nfast)
       plan.issue(sbase + j * C::BUF, j);
     else if (j < nblk)
-      issue_block<Q, N, R, LDN>(sbase + j * C::BUF, x, Bm, dA_cs, dt_T, c0 + j / C::BPC,
+      issue_block<Q, N, R, LDN, ALT>(sbase + j * C::BUF, x, Bm, dA_cs, dt_T, c0 + j / C::BPC,
                                 j % C::BPC, b, h0, g, L, H, G, nc, ncol0);
   }
 
@@ -367,7 +389,7 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
       if (REPLAY) {
         const int j0 = max(0, i + 2 - C::NBUF);
         const int starts = (i - 1) / C::BPC - (j0 - 1 + C::BPC) / C::BPC + 1;  // j0 <= j <= i-1, j % BPC == 0
-        newer += 4 * R * (i > j0 ? max(starts, 0) : 0);
+        newer += 4 * R * (i > j0 ? max(starts, 0) : 0);  // store_hst: 4 per head tile
       }
     }
     asm volatile("" ::: "memory");
@@ -380,7 +402,7 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
       if (j < nfast)
         plan.issue(sbase + (j % C::NBUF) * C::BUF, j);
       else
-        issue_block<Q, N, R, LDN>(sbase + (j % C::NBUF) * C::BUF, x, Bm, dA_cs, dt_T,
+        issue_block<Q, N, R, LDN, ALT>(sbase + (j % C::NBUF) * C::BUF, x, Bm, dA_cs, dt_T,
                                   c0 + j / C::BPC, j % C::BPC, b, h0, g, L, H, G, nc, ncol0);
     }
     unsigned char* cur = smem + (i % C::NBUF) * C::BUF;
@@ -417,12 +439,18 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
 #pragma unroll
       for (int v = 0; v < R / HPW; ++v) {
         const int m = hh * (R / HPW) + v;
-        const int bc = 4 * tile_cols<C::NW, R>(w, m) + (L16 & 3);
+        // tile nt, MFMA row i: ALT n = 32 tile_cols + 16 nt + i (lane L16
+        // points at chunk 4 tile_cols + 2 nt + (L16 % 4) / 2, half L16 % 2);
+        // else n = 32 tile_cols + 8 (i / 4) + 4 nt + i % 4 (chunk
+        // 4 tile_cols + L16 % 4, half nt)
         bf16x8 bop[2];
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const bf16* pa = (const bf16*)(bsm + ra * (2 * N) + sb<N>(ra, bc) * 16 + 8 * nt);
-          const bf16* pb = (const bf16*)(bsm + rb * (2 * N) + sb<N>(rb, bc) * 16 + 8 * nt);
+          const int bc = ALT ? 4 * tile_cols<C::NW, R>(w, m) + 2 * nt + ((L16 & 3) >> 1)
+                             : 4 * tile_cols<C::NW, R>(w, m) + (L16 & 3);
+          const int hb = ALT ? 8 * (L16 & 1) : 8 * nt;
+          const bf16* pa = (const bf16*)(bsm + ra * (2 * N) + sb<N, ALT>(ra, bc) * 16 + hb);
+          const bf16* pb = (const bf16*)(bsm + rb * (2 * N) + sb<N, ALT>(rb, bc) * 16 + hb);
           bop[nt] = cat(lds_read_tr(pa), lds_read_tr(pb));
         }
 #pragma unroll
@@ -440,13 +468,13 @@ __global__ void __launch_bounds__((SpanCfg<Q, N, R, OCCT>::NT), (SpanCfg<Q, N, R
 #pragma unroll
     for (int m = 0; m < R; ++m) {
       const int r = tile_head<C::NW, R>(w, m);
-      const int ncol = 32 * tile_cols<C::NW, R>(w, m) + 8 * grp;
+      const int ncol = 32 * tile_cols<C::NW, R>(w, m);
       float* sst = span_states + (((int64_t)b * ng + s) * H + h0 + r) * 64 * LDN + ncol0;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          *(f32x4*)(sst + (16 * pt + L16) * LDN + ncol + 4 * nt) = acc[m][nt][pt];
+          *(f32x4*)(sst + (16 * pt + L16) * LDN + ncol + acc_col<ALT>(nt, grp)) = acc[m][nt][pt];
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
