@@ -118,22 +118,47 @@ int hip_status(hipError_t e, const char* where) {
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace of the fused forward: dA_cs and dt_T [B,H,nc,Q] f32, the per-chunk
-// states [B,nc,H,P,N] f32, (grouped path) the chunk-start states as bf16, and
-// (grouped path at state size 512) the first column half's float32 y.
+// Workspace of mamba2_ssd_forward, exactly what its path uses (256-byte
+// aligned pieces): dA_cs and dt_T [B,H,nc,Q] f32; then
+//   split path: the per-chunk states [B,nc,H,P,N] f32, (grouped output
+//     stage) the chunk-start states as bf16 and (state size 512) the first
+//     column half's y as bf16;
+//   span path (K > 0): the span states [B,ng,H,P,N] f32 and span log2 decays
+//     [B,H,ng], then, unless span_scan runs, the bf16 chunk-start states and
+//     (state size 512) the first column half's y.
+// The opt-in one-kernel forward (mamba2_ssd_forward_fused) carves its own
+// layout (three [B,H,nc,Q] f32 arrays and the bf16 chunk-start states) from
+// the same workspace, so `total` covers that too where it is supported.
 struct Workspace {
   bool grouped;
-  size_t cs_bytes, st_bytes, hst_bytes, part_bytes, total;
+  int K, Rs;  // span length (0: split path) and span_scan heads (0: replay)
+  size_t cs_bytes, st_bytes, span_bytes, hst_bytes, part_bytes, total;
 };
 
 Workspace plan(const m2::Dims& d) {
   Workspace w;
   w.grouped = m2::grouped_scan_supported(d);
+  w.K = w.grouped ? m2::span_chunks(d) : 0;
+  w.Rs = w.K ? m2::span_scan_heads(d, w.K) : 0;
   w.cs_bytes = round256((size_t)(d.B * d.H * d.nc * d.Q) * sizeof(float));
-  w.st_bytes = round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * sizeof(float));
-  w.hst_bytes = w.grouped ? round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * 2) : 0;
-  w.part_bytes = w.grouped ? round256(m2::grouped_scan_part_bytes(d)) : 0;
+  const size_t hst = round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * 2);
+  if (w.K) {
+    const int64_t ng = (d.nc + w.K - 1) / w.K;
+    w.span_bytes = round256(m2::span_states_bytes(d, w.K));
+    w.st_bytes = w.span_bytes + round256((size_t)(d.B * d.H * ng) * sizeof(float));
+    w.hst_bytes = w.Rs ? 0 : hst;
+    w.part_bytes = w.Rs ? 0 : round256(m2::grouped_scan_part_bytes(d));
+  } else {
+    w.span_bytes = 0;
+    w.st_bytes = round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * sizeof(float));
+    w.hst_bytes = w.grouped ? hst : 0;
+    w.part_bytes = w.grouped ? round256(m2::grouped_scan_part_bytes(d)) : 0;
+  }
   w.total = 2 * w.cs_bytes + w.st_bytes + w.hst_bytes + w.part_bytes;
+  if (m2::fused_state_supported(d)) {
+    const size_t fused = 3 * w.cs_bytes + hst;
+    if (fused > w.total) w.total = fused;
+  }
   return w;
 }
 
@@ -148,22 +173,20 @@ int enqueue_forward(const m2::Dims& d, const void* x, const void* dt, const floa
   float* dt_T = (float*)(ws + w.cs_bytes);
   float* states = (float*)(ws + 2 * w.cs_bytes);
   void* hst = ws + 2 * w.cs_bytes + w.st_bytes;
-  float* part = w.part_bytes ? (float*)(ws + 2 * w.cs_bytes + w.st_bytes + w.hst_bytes) : nullptr;
+  void* part = w.part_bytes ? (void*)(ws + 2 * w.cs_bytes + w.st_bytes + w.hst_bytes) : nullptr;
   hipError_t e = hipSuccess;
   if (ev) e = hipEventRecord(ev[0], s);
   if (e == hipSuccess) e = m2::launch_chunk_cumsum(d, dt, A, dA_cs, dt_T, s);
   if (e != hipSuccess) return hip_status(e, "chunk_cumsum launch");
   if (ev) e = hipEventRecord(ev[1], s);
-  const int K = w.grouped ? m2::span_chunks(d) : 0;
-  const size_t span_bytes = K ? round256(m2::span_states_bytes(d, K)) : 0;
-  if (K && span_bytes + round256((size_t)(d.B * d.H * ((d.nc + K - 1) / K)) * 4) <= w.st_bytes) {
+  const int K = w.K;
+  if (K) {
     // fwd_pass_state over spans: span-end states (stage slot 1), then the
     // jump across spans and the replay that writes the chunk-start states
-    // (stage slot 2)
-    float* span_decay = (float*)((char*)states + span_bytes);
-    // the replay fused with the output stage where span_scan covers the
-    // sizes (stage slots: span-end states, jump across spans, span_scan)
-    const int Rs = m2::span_scan_heads(d, K);
+    // (stage slot 2); or, where span_scan covers the sizes, the jump alone
+    // (slot 2) and span_scan, the replay fused with the output stage (slot 3)
+    float* span_decay = (float*)((char*)states + w.span_bytes);
+    const int Rs = w.Rs;
     if (e == hipSuccess)
       e = m2::launch_fwd_pass_state_span(d, K, x, B, dA_cs, dt_T, init_state, states, span_decay,
                                          hst, final_state, s, ev ? ev[2] : nullptr, Rs == 0);

@@ -31,10 +31,7 @@ namespace m2 {
 
 namespace {
 
-#ifndef M2_HOP_AHEAD
-#define M2_HOP_AHEAD 3
-#endif
-constexpr int kHopAhead = M2_HOP_AHEAD;  // state-operand reads in flight ahead of the MFMAs
+constexpr int kHopAhead = 3;  // state-operand reads in flight ahead of the MFMAs
 
 enum ScanMode { kWhole = 0, kFirstHalf = 1, kSecondHalf = 2 };
 
@@ -238,38 +235,39 @@ __device__ __forceinline__ void store_tile(const f32x4 (&Yt)[P / 16], int t, bf1
   }
 }
 
-// The first half pass's float32 y: the same lane layout as store_tile,
-// 4 PT consecutive p of one token per lane (4 PT * 4 bytes, 16-byte stores),
-// in a [B, L, H, P] float32 buffer.
+// The first half pass's y, rounded to bfloat16 for the second pass (at
+// state size 512 y = first half + second half's carried-state term; a
+// float32 hand-over would move 8 bytes per output element through HBM, this
+// moves 4): the same lane layout as store_tile, 4 PT consecutive p of one
+// token per lane, in a [B, L, H, P] bfloat16 buffer.
 template <int P>
 __device__ __forceinline__ void store_part(const f32x4 (&Yt)[P / 16], int t,
-                                           float* __restrict__ part, int64_t ybase, int H,
+                                           bf16* __restrict__ part, int64_t ybase, int H,
                                            int64_t valid) {
-  constexpr int PT = P / 16;
-  const int lane = lane_id();
-  const int L16 = lane & 15, grp = lane >> 4;
-  const int i = 16 * t + L16;
-  if (i < valid) {
-    float* dst = part + (ybase + (int64_t)i * H) * P + 4 * PT * grp;
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) *(f32x4*)(dst + 4 * pt) = Yt[pt];
-  }
+  store_tile<P>(Yt, t, part, ybase, H, valid);
 }
 
-// Adds the first half pass's float32 y to one i-tile (rows past the
-// sequence end are neither read nor stored).
+// Adds the first half pass's y to one i-tile (rows past the sequence end are
+// neither read nor stored).
 template <int P>
 __device__ __forceinline__ void add_part(f32x4 (&Yt)[P / 16], int t,
-                                         const float* __restrict__ part, int64_t ybase, int H,
+                                         const bf16* __restrict__ part, int64_t ybase, int H,
                                          int64_t valid) {
   constexpr int PT = P / 16;
   const int lane = lane_id();
   const int L16 = lane & 15, grp = lane >> 4;
   const int i = 16 * t + L16;
   if (i < valid) {
-    const float* src = part + (ybase + (int64_t)i * H) * P + 4 * PT * grp;
+    const bf16* src = part + (ybase + (int64_t)i * H) * P + 4 * PT * grp;
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) Yt[pt] += *(const f32x4*)(src + 4 * pt);
+    for (int pt = 0; pt < PT; pt += 2) {
+      const bf16x8 v = *(const bf16x8*)(src + 4 * pt);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Yt[pt][e] += bf2f(v[e]);
+        Yt[pt + 1][e] += bf2f(v[4 + e]);
+      }
+    }
   }
 }
 
@@ -278,7 +276,7 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
     const float* __restrict__ dA_cs, const float* __restrict__ dt_T,
     const bf16* __restrict__ hst, const float* __restrict__ Dv, bf16* __restrict__ y,
-    float* __restrict__ part, int L, int H, int G, int nc, int hpw, int slices, int n0) {
+    bf16* __restrict__ part, int L, int H, int G, int nc, int hpw, int slices, int n0) {
   using K = GCfg<P, Q, N>;
   constexpr int QT = K::QT, PT = K::PT, NBLK = K::NBLK, SROW = K::SROW;
   // rows of B, C and the start states hold ldn columns; G^T runs over all of
@@ -465,7 +463,7 @@ int cu_count() {
 template <int P, int Q, int N, int MODE>
 hipError_t launch_grouped(const Dims& d, const void* x, const void* B, const void* C,
                           const float* dA_cs, const float* dt_T, const void* hst, const float* D,
-                          void* y, float* part, int n0, hipStream_t s) {
+                          void* y, void* part, int n0, hipStream_t s) {
   using K = GCfg<P, Q, N>;
   auto kern = chunk_scan_grouped_kernel<P, Q, N, MODE>;
   static const hipError_t attr = hipFuncSetAttribute(
@@ -482,14 +480,14 @@ hipError_t launch_grouped(const Dims& d, const void* x, const void* B, const voi
   const int64_t grid = d.B * d.nc * d.G * slices;
   kern<<<(unsigned)grid, Q * 2, K::LDS, s>>>(
       (const bf16*)x, (const bf16*)B, (const bf16*)C, dA_cs, dt_T, (const bf16*)hst, D,
-      (bf16*)y, part, (int)d.L, (int)d.H, (int)d.G, (int)d.nc, (int)hpw, (int)slices, n0);
+      (bf16*)y, (bf16*)part, (int)d.L, (int)d.H, (int)d.G, (int)d.nc, (int)hpw, (int)slices, n0);
   return hipGetLastError();
 }
 
 template <int Q>
 hipError_t launch_grouped_n(const Dims& d, const void* x, const void* B, const void* C,
                             const float* dA_cs, const float* dt_T, const void* hst,
-                            const float* D, void* y, float* part, hipStream_t s) {
+                            const float* D, void* y, void* part, hipStream_t s) {
   switch (d.N) {
     case 64: return launch_grouped<64, Q, 64, kWhole>(d, x, B, C, dA_cs, dt_T, hst, D, y, nullptr, 0, s);
     case 128: return launch_grouped<64, Q, 128, kWhole>(d, x, B, C, dA_cs, dt_T, hst, D, y, nullptr, 0, s);
@@ -514,12 +512,12 @@ bool grouped_scan_supported(const Dims& d) {
 }
 
 size_t grouped_scan_part_bytes(const Dims& d) {
-  return d.N == 512 ? (size_t)(d.B * d.L * d.H * d.P) * sizeof(float) : 0;
+  return d.N == 512 ? (size_t)(d.B * d.L * d.H * d.P) * 2 : 0;
 }
 
 hipError_t launch_chunk_scan_grouped(const Dims& d, const void* x, const void* B, const void* C,
                                      const float* dA_cs, const float* dt_T, const void* hst,
-                                     const float* D, void* y, float* part, hipStream_t s) {
+                                     const float* D, void* y, void* part, hipStream_t s) {
   switch (d.Q) {
     case 64: return launch_grouped_n<64>(d, x, B, C, dA_cs, dt_T, hst, D, y, part, s);
     case 128: return launch_grouped_n<128>(d, x, B, C, dA_cs, dt_T, hst, D, y, part, s);

@@ -34,11 +34,11 @@ hipError_t launch_chunk_state_grouped(const Dims& d, const void* x, const void* 
                                       const float* dA_cs, const float* dt_T, float* states,
                                       hipStream_t s);
 // State size 512 runs as two passes over column halves and needs `part`, a
-// float32 [B, L, H, P] scratch of grouped_scan_part_bytes(d) (else NULL).
+// bfloat16 [B, L, H, P] scratch of grouped_scan_part_bytes(d) (else NULL).
 size_t grouped_scan_part_bytes(const Dims& d);
 hipError_t launch_chunk_scan_grouped(const Dims& d, const void* x, const void* B, const void* C,
                                      const float* dA_cs, const float* dt_T, const void* hst,
-                                     const float* D, void* y, float* part, hipStream_t s);
+                                     const float* D, void* y, void* part, hipStream_t s);
 
 // Backward pass (bfloat16, P = 64, N in {64, 128, 256}, Q in {64, 128, 256}).
 bool backward_supported(const Dims& d);

@@ -45,15 +45,9 @@ namespace m2 {
 namespace {
 
 // Most heads per workgroup, and workgroups per CU the LDS ring and the
-// register budget are sized for.
-#ifndef M2_SPAN_HEADS
-#define M2_SPAN_HEADS 4
-#endif
-#ifndef M2_SPAN_OCC
-#define M2_SPAN_OCC 1
-#endif
-constexpr int kSpanHeads = M2_SPAN_HEADS;
-constexpr int kSpanOcc = M2_SPAN_OCC;
+// register budget are sized for by default.
+constexpr int kSpanHeads = 4;
+constexpr int kSpanOcc = 1;
 
 template <int Q, int N, int R, int OCCT = kSpanOcc>
 struct SpanCfg {

@@ -79,9 +79,28 @@ def test_workspace_bytes():
     nc = 256
     cs = 1 * 32 * nc * 256 * 4
     st = 1 * nc * 32 * 64 * 256 * 4
-    # headdim 64 with dstate 256 runs the grouped output stage, which also keeps
-    # the chunk-start states as bfloat16
-    assert m2.mamba2_ssd_workspace_bytes(d) == 2 * cs + st + st // 2
+    # headdim 64 with dstate 256 at this length runs fwd_pass_state over spans
+    # of 8 chunks (the host has no device here, so the library assumes 256 CUs):
+    # float32 span states (an eighth of the per-chunk states), the span decays
+    # (32 heads x 32 spans, rounded up to 256 bytes... 4096), and the bfloat16
+    # chunk-start states for the grouped output stage
+    assert m2.mamba2_ssd_workspace_bytes(d) == 2 * cs + st // 8 + 4096 + st // 2
+    # state size 512: the first column half's y as bfloat16 too (workload of
+    # L = 256K, G = 4)
+    d4 = _dims(seqlen=262144, nheads=32, dstate=512, ngroups=4)
+    nc4 = 1024
+    cs4 = 32 * nc4 * 256 * 4
+    st4 = nc4 * 32 * 64 * 512 * 4
+    assert m2.mamba2_ssd_workspace_bytes(d4) == (2 * cs4 + st4 // 8 + 32 * 128 * 4 + st4 // 2
+                                                + 262144 * 32 * 64 * 2)
+    # state size 128 on the span path runs span_scan (no chunk-start states:
+    # 2 cs + st5 / 8 + 4096), but the same workspace also serves the opt-in
+    # one-kernel forward (three sum arrays and the bfloat16 chunk-start states),
+    # the larger of the two here
+    d5 = _dims(seqlen=65536, nheads=32, dstate=128)
+    st5 = nc * 32 * 64 * 128 * 4
+    assert 2 * cs + st5 // 8 + 4096 < 3 * cs + st5 // 2
+    assert m2.mamba2_ssd_workspace_bytes(d5) == 3 * cs + st5 // 2
     # ragged sequence rounds chunks up
     d2 = _dims(seqlen=1000)
     assert m2.mamba2_ssd_workspace_bytes(d2) == 2 * (8 * 4 * 256 * 4) + 4 * 8 * 64 * 64 * 6
