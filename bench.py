@@ -59,6 +59,23 @@ def span_plan(w, cus=256):
     return None
 
 
+def workload(name):
+    """A named workload, or a shape of the sequence-length x state-size sweep
+    named sweep_L<k>k_N<n> (batch 1, 32 heads of 64, one B/C group, chunk 256,
+    bf16, no initial state, as --sweep runs it)."""
+    import ssd_inputs
+    if name in ssd_inputs.WORKLOADS:
+        return ssd_inputs.WORKLOADS[name]
+    m = re.fullmatch(r"sweep_L(\d+)k_N(\d+)", name)
+    if not m:
+        raise SystemExit(f"unknown workload {name!r}: one of {list(ssd_inputs.WORKLOADS)} "
+                         "or sweep_L<k>k_N<n>")
+    L, N = int(m.group(1)) * 1024, int(m.group(2))
+    return ssd_inputs.custom(name=name, batch=1, seqlen=L, nheads=32, headdim=64, dstate=N,
+                             ngroups=1, chunk_size=256, dtype="bf16", init_state=False,
+                             seed=2000 + N + L // 1024)
+
+
 def scan_plan(w, cus=256):
     """Heads per workgroup of span_scan (the span replay fused with the output
     stage), or None where the forward runs the replay and the grouped
@@ -188,7 +205,7 @@ def main():
     import ssd_inputs
     import state_space_sequence_02_amd as m2
 
-    w = ssd_inputs.WORKLOADS[args.workload]
+    w = workload(args.workload)
     inp = ssd_inputs.make_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -359,7 +376,7 @@ def fused_state_bench(args):
     import ssd_inputs
     import state_space_sequence_02_amd as m2
 
-    w = ssd_inputs.WORKLOADS[args.workload]
+    w = workload(args.workload)
     inp = ssd_inputs.make_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -700,7 +717,7 @@ def backward_bench(args):
     import ssd_inputs
     import state_space_sequence_02_amd as m2
 
-    w = ssd_inputs.WORKLOADS[args.workload]
+    w = workload(args.workload)
     inp = ssd_inputs.make_inputs(w)
     cot = ssd_inputs.make_cotangents(w)
     dev = torch.device("cuda:0")
