@@ -52,8 +52,12 @@
  * data): A <= 0, dt >= 0 and every input finite - the decay regime the
  * method describes (decay rate times time interval).
  * Supported sizes: Q in {16, 32, 64, 128, 256} for float32 and
- * {64, 128, 256} for bfloat16; bfloat16 also needs P in {32, 64, 128} and
- * N a multiple of 64 with N <= 512.  Other sizes give MAMBA2_ERR_UNSUPPORTED.
+ * {64, 128, 256} for bfloat16; bfloat16 also needs P and N multiples of 16
+ * with P <= 128 and N <= 512 (the MFMA tile is 16 wide; larger states do not
+ * fit one workgroup's registers and LDS).  The fastest kernels (shared B/C
+ * operands across the heads of a group, spans of chunks) cover bfloat16
+ * with P = 64 and N in {64, 128, 256, 512}; other supported sizes run
+ * per-head kernels.  Other sizes give MAMBA2_ERR_UNSUPPORTED.
  */
 #ifndef MAMBA2_SSD_H_
 #define MAMBA2_SSD_H_
@@ -162,12 +166,18 @@ size_t mamba2_ssd_workspace_bytes(const mamba2_dims* dims);
  * return are unspecified).  init_state and D may be NULL; final_state may
  * be NULL (not written).  Outputs y [B,L,H,P] (dtype of dims) and
  * final_state [B,H,P,N] float32.  fwd_pass_state runs as chunk_state ->
- * state_passing, or, for bfloat16 with headdim 64, dstate 64/128/256 and
- * enough (batch, head, span) work to fill the device, over spans of 8 (or
- * 4) chunks (devotd.net news item, section 2: the same jump across chunks,
- * taken span by span): the state after each span from a zero start, the
- * jump across spans, then each span replayed from its start state to give
- * the chunk-start states.  Both give the same result up to rounding order.
+ * state_passing, or, for bfloat16 with headdim 64, dstate 64/128/256/512
+ * and enough (batch, head, span) work to fill the device, over spans of 8
+ * (or 4) chunks (devotd.net news item, section 2: the same jump across
+ * chunks, taken span by span): the state after each span from a zero start,
+ * the jump across spans, then each span replayed from its start state.  At
+ * dstate 256 and 512 the replay writes bfloat16 chunk-start states for
+ * chunk_scan; at dstate 64 and 128, with an even number of heads per group,
+ * one kernel replays each span and forms its outputs in the same pass, so
+ * the chunk-start states stay on chip.  At dstate 512 the output stage runs
+ * over two halves of the state columns and the first hands its partial y to
+ * the second in bfloat16 (one more rounding of that partial).  All forms
+ * give the same result up to rounding.
  */
 int mamba2_ssd_forward(const mamba2_dims* dims, const void* x, const void* dt,
                        const float* A, const void* B, const void* C, const float* D,
