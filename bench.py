@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "SSD forward tokens/s at L=64K,N=256 on 1 MI355X; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, TFLOP/s
+FP32_VALU_PEAK_TFLOPS = 157.3  # float32 vector FMA, TFLOP/s
 RIDGE = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 STAGES = ("chunk_cumsum", "chunk_state", "state_passing", "chunk_scan")
 
@@ -707,6 +708,28 @@ def backward_model(w):
     return m
 
 
+def backward_fast(w):
+    """Whether the MFMA backward kernels cover the workload (else the generic
+    float32 backward runs)."""
+    return (w.dtype == "bf16" and w.headdim == 64 and w.dstate in (64, 128, 256)
+            and w.chunk_size in (64, 128, 256))
+
+
+def generic_backward_flops(w):
+    """Flops the generic backward's contractions issue (float32 FMAs, 2 flops
+    each; the causal triangles counted at half the square, the group-shared
+    C B^T once per group): adjoint states, the g B^T and h C^T products, the
+    in-chunk dU contraction, dy x^T for the decay gradient, and dB, dC (their
+    dy x^T tiles recomputed once per 64 state columns)."""
+    B, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
+    tok = B * L
+    per_head = (3 * P * N          # adjoint states, g B^T, h C^T
+                + Q / 2 * P        # dU in-chunk
+                + Q / 2 * P        # dy x^T for the decay gradient
+                + 2 * (P * N + Q / 2 * P * -(-N // 64) + Q / 2 * N))  # dC and dB
+    return 2 * tok * (H * per_head + G * Q / 2 * N)
+
+
 def backward_bench(args):
     """Backward pass over the workload: tokens/s of one mamba2_ssd_backward
     (it recomputes the forward's chunk states inside), per-stage times from
@@ -746,6 +769,28 @@ def backward_bench(args):
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    if not backward_fast(w):
+        # generic backward: one pass of float32 vector-ALU kernels, measured as
+        # a whole against the fp32 vector peak
+        fl = generic_backward_flops(w)
+        achieved = fl / (ms * 1e-3) / 1e12
+        out = {
+            "metric": f"SSD backward tokens/s, {w.name} on 1 MI355X (forward states recomputed)",
+            "value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32" if w.dtype == "f32" else "f32 (bf16 operands)", "data": "synthetic",
+            "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen,
+                       "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate,
+                       "ngroups": w.ngroups, "chunk_size": w.chunk_size, "path": "generic",
+                       "parallelism": "none (1 GPU)"},
+            "roofline": {"kernel": "generic backward (all kernels)", "bound": "alu",
+                         "achieved": achieved, "peak": FP32_VALU_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / FP32_VALU_PEAK_TFLOPS,
+                         "traffic": None, "algorithmic_flops": fl},
+        }
+        print(json.dumps(out), flush=True)
+        return
     ssum = [0.0] * len(BWD_STAGES)
     for _ in range(args.steps):
         ssum = [u + v for u, v in zip(ssum, m2.mamba2_ssd_backward_profile(*a))]

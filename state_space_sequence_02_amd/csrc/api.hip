@@ -283,16 +283,33 @@ int scratch_on_current_device(void** out) {
 // states, final state) and its own (bf16 end-of-chunk gradients, carried-state
 // and boundary dot-product parts, the groups' summed interaction matrices,
 // per-chunk dA and dD parts).
+// Backward workspace.  MFMA path (backward_supported): dA_cs, dt_T, the
+// float32 per-chunk states (then the adjoint states), bf16 chunk-start
+// states and chunk-end gradients, the recomputed final state, and the
+// kernels' partial sums.  Generic path: dA_cs, dt_T, the float32 chunk-start
+// states and adjoint states / chunk-end gradients, then the scratch of
+// generic_backward_sizes (float32).
 struct BwdWorkspace {
+  bool fast;
   size_t cs, st, hst, fin, th, wsum, rsum, dots, part, total;
   int64_t wph;
+  m2::GenericBwdSizes gen;
 };
 
 BwdWorkspace plan_backward(const m2::Dims& d) {
-  BwdWorkspace w;
-  w.wph = m2::state_reverse_waves_per_head(d);
+  BwdWorkspace w = {};
+  w.fast = m2::backward_supported(d);
   w.cs = round256((size_t)(d.B * d.H * d.nc * d.Q) * sizeof(float));
   w.st = round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * sizeof(float));
+  if (!w.fast) {
+    w.gen = m2::generic_backward_sizes(d);
+    const m2::GenericBwdSizes& g = w.gen;
+    w.total = 2 * w.cs + 2 * w.st +
+              round256(g.vg * 4) + round256(g.thp * 4) + round256(g.xup * 4) +
+              round256(g.ghp * 4) + round256(g.cb * 4) + 2 * round256(g.part * 4);
+    return w;
+  }
+  w.wph = m2::state_reverse_waves_per_head(d);
   w.hst = round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * 2);
   w.fin = round256((size_t)(d.B * d.H * d.P * d.N) * sizeof(float));
   w.th = round256((size_t)(d.B * d.nc * d.H * (d.N / 64) * d.Q) * sizeof(float));
@@ -304,6 +321,48 @@ BwdWorkspace plan_backward(const m2::Dims& d) {
   return w;
 }
 
+// The generic backward: the forward's per-chunk states recomputed (float32
+// chunk-start states), then chunk_bwd_generic.hip.
+int enqueue_backward_generic(const m2::Dims& d, const BwdWorkspace& w, const void* x,
+                             const void* dt, const float* A, const void* B, const void* C,
+                             const float* D, const float* init_state, const void* dy,
+                             const float* dfinal, void* dx, void* ddt, float* dA, void* dB,
+                             void* dC, float* dD, float* dinit, void* workspace, hipStream_t s) {
+  char* p = (char*)workspace;
+  float* dA_cs = (float*)p;
+  p += w.cs;
+  float* dt_T = (float*)p;
+  p += w.cs;
+  float* hs = (float*)p;
+  p += w.st;
+  float* E = (float*)p;
+  p += w.st;
+  m2::GenericBwdScratch g;
+  auto take = [&](size_t n) {
+    float* q = (float*)p;
+    p += round256(n * 4);
+    return q;
+  };
+  g.vg = take(w.gen.vg);
+  g.thp = take(w.gen.thp);
+  g.xup = take(w.gen.xup);
+  g.ghp = take(w.gen.ghp);
+  g.cb = take(w.gen.cb);
+  g.dA_part = take(w.gen.part);
+  g.dD_part = take(w.gen.part);
+  hipError_t e = m2::launch_chunk_cumsum(d, dt, A, dA_cs, dt_T, s);
+  if (e == hipSuccess)
+    e = m2::grouped_state_supported(d) ? m2::launch_chunk_state_grouped(d, x, B, dA_cs, dt_T, hs, s)
+                                       : m2::launch_chunk_state(d, x, B, dA_cs, dt_T, hs, s);
+  if (e == hipSuccess) e = m2::launch_state_passing(d, hs, dA_cs, init_state, nullptr, s);
+  if (e == hipSuccess)
+    e = m2::launch_backward_generic(d, x, dy, B, C, dA_cs, dt_T, hs, E, dfinal, dinit, A, D, dx,
+                                    ddt, dB, dC, g, s);
+  if (e == hipSuccess)
+    e = m2::launch_bwd_param_sums(d, g.dA_part, g.dD_part, dA, D ? dD : nullptr, s);
+  return hip_status(e, "backward launch");
+}
+
 constexpr int kBwdStages = 8;
 
 int enqueue_backward(const m2::Dims& d, const void* x, const void* dt, const float* A,
@@ -312,6 +371,22 @@ int enqueue_backward(const m2::Dims& d, const void* x, const void* dt, const flo
                      void* dB, void* dC, float* dD, float* dinit, void* workspace,
                      hipStream_t s, hipEvent_t* ev) {
   const BwdWorkspace w = plan_backward(d);
+  if (!w.fast) {
+    if (ev) {  // one stage: the whole generic pass
+      hipError_t e = hipEventRecord(ev[0], s);
+      int rc = e == hipSuccess ? MAMBA2_OK : hip_status(e, "event record");
+      if (rc == MAMBA2_OK)
+        rc = enqueue_backward_generic(d, w, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt,
+                                      dA, dB, dC, dD, dinit, workspace, s);
+      for (int i = 1; i <= kBwdStages && rc == MAMBA2_OK; ++i) {
+        e = hipEventRecord(ev[i], s);
+        if (e != hipSuccess) rc = hip_status(e, "event record");
+      }
+      return rc;
+    }
+    return enqueue_backward_generic(d, w, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA,
+                                    dB, dC, dD, dinit, workspace, s);
+  }
   char* p = (char*)workspace;
   float* dA_cs = (float*)p;
   p += w.cs;
@@ -377,10 +452,6 @@ int check_backward_args(const mamba2_dims* dims, m2::Dims* d, const void* x, con
                         void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD,
                         float* dinit, void* workspace, size_t workspace_bytes) {
   CHECK(validate(dims, d));
-  if (!m2::backward_supported(*d))
-    return fail(MAMBA2_ERR_UNSUPPORTED,
-                "backward needs bfloat16, headdim 64, dstate 64/128/256 and chunk_size "
-                "64/128/256");
   CHECK(need(x, "x"));
   CHECK(need(dt, "dt"));
   CHECK(need(A, "A"));
@@ -398,7 +469,7 @@ int check_backward_args(const mamba2_dims* dims, m2::Dims* d, const void* x, con
   if (D) CHECK(need(dD, "dD"));
   CHECK(maybe(dinit, "dinit"));
   const BwdWorkspace w = plan_backward(*d);
-  if (w.wph > 64)  // the dx kernel sums the boundary parts with one wavefront
+  if (w.fast && w.wph > 64)  // the dx kernel sums the boundary parts with one wavefront
     return fail(MAMBA2_ERR_UNSUPPORTED, "state too large for the backward pass");
   if (!workspace) return fail(MAMBA2_ERR_WORKSPACE, "workspace is NULL");
   if (((uintptr_t)workspace & 255u) != 0)
@@ -471,7 +542,7 @@ int mamba2_ssd_forward_fused(const mamba2_dims* dims, const void* x, const void*
 
 size_t mamba2_ssd_backward_workspace_bytes(const mamba2_dims* dims) {
   m2::Dims d;
-  if (validate(dims, &d) != MAMBA2_OK || !m2::backward_supported(d)) return 0;
+  if (validate(dims, &d) != MAMBA2_OK) return 0;
   return plan_backward(d).total;
 }
 

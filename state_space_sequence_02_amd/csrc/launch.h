@@ -68,6 +68,24 @@ hipError_t launch_chunk_bwd_dx(const Dims& d, const void* x, const void* dy, con
 hipError_t launch_bwd_param_sums(const Dims& d, const float* dA_part, const float* dD_part,
                                  float* dA, float* dD, hipStream_t s);
 
+// Backward pass for the sizes backward_supported() rejects (chunk_bwd_generic.hip):
+// float32 arithmetic on the vector ALU, any size the forward accepts with
+// Q <= 256.  hs: the float32 chunk-start states [B,nc,H,P,N] (from
+// chunk_state + state_passing); E: [B,nc,H,P,N] float32 scratch (left holding
+// the gradient at every chunk end); the scratch below in float32 elements.
+struct GenericBwdSizes {
+  size_t vg, thp, xup, ghp, cb, part;
+};
+GenericBwdSizes generic_backward_sizes(const Dims& d);
+struct GenericBwdScratch {
+  float *vg, *thp, *xup, *ghp, *cb, *dA_part, *dD_part;
+};
+hipError_t launch_backward_generic(const Dims& d, const void* x, const void* dy, const void* B,
+                                   const void* C, const float* dA_cs, const float* dt_T,
+                                   float* hs, float* E, const float* dfinal, float* dinit,
+                                   const float* A, const float* D, void* dx, void* ddt, void* dB,
+                                   void* dC, const GenericBwdScratch& w, hipStream_t s);
+
 // fwd_pass_state as one kernel (bfloat16, P = 64, N in {64, 128, 256},
 // Q in {64, 128, 256}): chunk-start states to hst (bf16 [B,nc,H,P,N]) and the
 // final state, from the weights w_T = 2^(cs_last - cs_j) dt_j [B,H,nc,Q].

@@ -169,13 +169,25 @@ def test_backward_checks_on_host():
         args.update(over)
         return lib.mamba2_ssd_backward(ctypes.byref(dims), *args.values(), 0)
 
-    # float32 and headdim 32 are valid forward sizes the backward does not cover
+    # float32, headdim 32 and state size 512 take the generic backward: its
+    # workspace holds at least the cumulative sums, dt and two float32 state
+    # arrays, and its argument checks are those of the MFMA path
     for kw in (dict(dtype=m2.MAMBA2_DTYPE_F32, headdim=16, dstate=16, nheads=2, chunk_size=64),
                dict(headdim=32), dict(dstate=512)):
         dd = _dims(**kw)
         assert m2.mamba2_validate(dd) == m2.MAMBA2_OK
-        assert m2.mamba2_ssd_backward_workspace_bytes(dd) == 0
-        assert call(dd) == m2.MAMBA2_ERR_UNSUPPORTED and "backward" in m2.mamba2_last_error()
+        nc = -(-dd.seqlen // dd.chunk_size)
+        floor = 4 * (2 * dd.batch * dd.nheads * nc * dd.chunk_size +
+                     2 * dd.batch * nc * dd.nheads * dd.headdim * dd.dstate)
+        assert m2.mamba2_ssd_backward_workspace_bytes(dd) >= floor
+        assert call(dd, dx=None) == m2.MAMBA2_ERR_NULL and "dx" in m2.mamba2_last_error()
+        assert call(dd, dC=ok + 4) == m2.MAMBA2_ERR_ALIGN and "dC" in m2.mamba2_last_error()
+        need = m2.mamba2_ssd_backward_workspace_bytes(dd)
+        assert call(dd, wsb=need - 1) == m2.MAMBA2_ERR_WORKSPACE
+    # sizes the forward refuses stay refused
+    bad = _dims(headdim=40)
+    assert m2.mamba2_ssd_backward_workspace_bytes(bad) == 0
+    assert call(bad) == m2.MAMBA2_ERR_UNSUPPORTED
     assert call(d, dy=None) == m2.MAMBA2_ERR_NULL and "dy" in m2.mamba2_last_error()
     assert call(d, dB=ok + 2) == m2.MAMBA2_ERR_ALIGN and "dB" in m2.mamba2_last_error()
     # dD is required exactly when D is given

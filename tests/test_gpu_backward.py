@@ -147,6 +147,114 @@ def test_backward_writes_only_its_outputs(m2):
         assert torch.isfinite(views[k].float()).all(), k
 
 
+def _wg(name, L, H, P, N, G, Q, Bn=1, init=True, seed=0, dtype="bf16"):
+    return ssd_inputs.custom(name=name, batch=Bn, seqlen=L, nheads=H, headdim=P, dstate=N,
+                             ngroups=G, chunk_size=Q, dtype=dtype, init_state=init, seed=seed)
+
+
+# Sizes the MFMA backward does not cover run the generic backward (float32
+# arithmetic on the vector ALU): float32 inputs, head sizes other than 64,
+# state sizes other than 64/128/256 (512 included).  The shapes put 1 to 4
+# output tiles of 64 along the chunk, the head size and the state size, with
+# ragged tiles, ragged last chunks, a sequence shorter than one chunk and a
+# single token.
+GENERIC = [
+    _wg("gbwd_f32_Q64_P16_N32_G2_ragged", 200, 4, 16, 32, 2, 64, Bn=2, dtype="f32", seed=81),
+    _wg("gbwd_f32_Q16_P32_N16", 70, 2, 32, 16, 1, 16, dtype="f32", seed=82),
+    _wg("gbwd_f32_Q256_P80_N100", 300, 2, 80, 100, 1, 256, dtype="f32", init=False, seed=83),
+    _wg("gbwd_bf16_P32_N64", 300, 4, 32, 64, 2, 128, seed=84),
+    _wg("gbwd_bf16_P64_N512_G2", 600, 4, 64, 512, 2, 256, seed=85),
+    _wg("gbwd_bf16_P64_N512_Q64", 333, 4, 64, 512, 4, 64, Bn=2, seed=86),
+    _wg("gbwd_bf16_P128_N96", 257, 2, 128, 96, 1, 128, seed=87),
+    _wg("gbwd_bf16_P48_N208_short", 40, 3, 48, 208, 3, 64, seed=88),
+    _wg("gbwd_bf16_one_token_N512", 1, 2, 64, 512, 1, 64, seed=89),
+]
+GTOL = {"bf16": BT, "f32": TOL["f32"]}
+
+
+@pytest.mark.parametrize("w", GENERIC, ids=lambda w: w.name)
+def test_generic_backward_matches_oracle(m2, w):
+    say(f"backward (generic) {w.name}")
+    got, ref = _run(m2, w)
+    errs = _compare(got, ref, GTOL[w.dtype])
+    say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+def test_generic_backward_without_D_or_final_gradient(m2):
+    for w in (GENERIC[0], GENERIC[4]):
+        got, ref = _run(m2, w, with_D=False, with_dfinal=False)
+        assert got["dD"] is None
+        _compare(got, ref, GTOL[w.dtype])
+
+
+@pytest.mark.parametrize("w", [GENERIC[2], GENERIC[5]], ids=lambda w: w.name)
+def test_generic_backward_writes_only_its_outputs(m2, w):
+    inp = ssd_inputs.make_inputs(w)
+    cot = ssd_inputs.make_cotangents(w)
+    g = to_gpu(inp)
+    dims = m2.dims_of(g["x"], g["B"], w.chunk_size)
+    pad = 4096
+    bufs, views = {}, {}
+    for k, like in (("dx", g["x"]), ("ddt", g["dt"]), ("dB", g["B"]), ("dC", g["C"])):
+        n = like.numel()
+        bufs[k] = torch.full((n + 2 * pad,), 5.0, dtype=like.dtype, device="cuda")
+        views[k] = bufs[k][pad:pad + n].view(like.shape)
+    hw = w.nheads * w.headdim * w.dstate * w.batch
+    dinit_buf = torch.full((hw + 2 * pad,), 5.0, dtype=torch.float32, device="cuda")
+    dinit = dinit_buf[pad:pad + hw].view(w.batch, w.nheads, w.headdim, w.dstate)
+    need = m2.mamba2_ssd_backward_workspace_bytes(dims)
+    ws_buf = torch.full((need + 2 * pad,), 7, dtype=torch.uint8, device="cuda")
+    ws = ws_buf[pad:pad + need]
+    dA = torch.empty(w.nheads, dtype=torch.float32, device="cuda")
+    dD = torch.empty_like(dA)
+    m2.mamba2_ssd_backward(dims, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"],
+                           g["init_state"], cot["dy"].cuda(), cot["dfinal"].cuda(), views["dx"],
+                           views["ddt"], dA, views["dB"], views["dC"], dD, dinit, ws, need)
+    torch.cuda.synchronize()
+    for k, b in list(bufs.items()) + [("dinit", dinit_buf)]:
+        assert torch.all(b[:pad] == 5.0) and torch.all(b[-pad:] == 5.0), k
+    assert torch.all(ws_buf[:pad] == 7) and torch.all(ws_buf[-pad:] == 7)
+    for k, v in list(views.items()) + [("dinit", dinit)]:
+        assert torch.isfinite(v.float()).all(), k
+
+
+def test_generic_backward_multichunk_N512(m2):
+    """16 chunks of 256 at the largest state (N = 512), 8 heads in 2 groups:
+    the generic backward across many chunk boundaries."""
+    w = _wg("gbwd_long_L4096_N512", 4096, 8, 64, 512, 2, 256, seed=90)
+    say(f"backward (generic) {w.name}")
+    got, ref = _run(m2, w)
+    errs = _compare(got, ref)
+    say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+def test_generic_backward_fullsize_properties(m2):
+    """L = 262144, H = 32, P = 64, N = 512, G = 4, Q = 256 (the largest-state
+    workload) through the generic backward: finite gradients, dD equal to
+    sum(dy * x), and gradients homogeneous in the upstream gradient."""
+    w = ssd_inputs.custom(name="gbwd_full", batch=1, seqlen=262144, nheads=32, headdim=64,
+                          dstate=512, ngroups=4, chunk_size=256, init_state=False, seed=91)
+    say(f"backward (generic) {w.name}")
+    inp = ssd_inputs.make_inputs(w)
+    cot = ssd_inputs.make_cotangents(w)
+    g = to_gpu(inp)
+    dy = cot["dy"].cuda()
+    dfin = cot["dfinal"].cuda()
+    a = m2.ssd_backward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], None, dy, dfin,
+                        chunk_size=256)
+    torch.cuda.synchronize()
+    for k in NAMES:
+        assert torch.isfinite(a[k].float()).all(), k
+    dD_ref = (dy.double() * g["x"].double()).sum(dim=(0, 1, 3))
+    assert normwise(f64(a["dD"]), dD_ref.cpu().numpy()) <= 1e-4
+    b2 = m2.ssd_backward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], None, 2 * dy, 2 * dfin,
+                         chunk_size=256)
+    torch.cuda.synchronize()
+    for k in NAMES:
+        diff = (b2[k].float() != 2 * a[k].float()).sum().item()
+        assert diff <= 1e-6 * a[k].numel() + 1, (k, diff)
+
+
 def test_backward_fullsize_properties(m2):
     """L = 65536, H = 32, P = 64, N = 256, G = 1, Q = 256 (the long-sequence
     workload): gradients are finite; dD equals sum(dy * x) over the batch and
