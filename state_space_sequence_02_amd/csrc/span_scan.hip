@@ -69,14 +69,17 @@ struct ScanSpanCfg {
   static constexpr int TOT = XT + 2 * BT + 1;  // direct-to-LDS loads per block (workgroup)
   static constexpr int NJ = (TOT + NW - 1) / NW;  // most loads per wave per block
   static constexpr int STORES = 2 * HPW;     // y stores per wave per block
+  // per wave, per head: a block's decay tables (96 floats), after the ring
+  static constexpr int TABW = HPW * 96 * 4;
+  static constexpr int TAB = NW * TABW;
   static constexpr int depth() {
-    int nb = 160 * 1024 / BUF;
+    int nb = (160 * 1024 - TAB) / BUF;
     if (nb > 4) nb = 4;
     while (nb > 3 && NJ * (nb - 2) + STORES * (nb - 1) > 62) --nb;
     return nb;
   }
   static constexpr int NBUF = depth();
-  static constexpr int LDS = NBUF * BUF;
+  static constexpr int LDS = NBUF * BUF + TAB;
   static_assert(HPW == 1 || HPW == 2, "heads per wave");
   static_assert(N == 64 || N == 128, "state size");
   static_assert(NBUF >= 3 && NJ * (NBUF - 2) + STORES * (NBUF - 1) <= 62, "ring depth");
@@ -106,10 +109,17 @@ __device__ __forceinline__ bf16x8 to_bf8(f32x4 lo, f32x4 hi) {
 
 // 16-byte direct-to-LDS load from a wave-uniform base plus this lane's
 // 32-bit byte offset (saddr form: the base stays in scalar registers);
-// otherwise as dma16.
+// otherwise as dma16.  A vector memory instruction that reads an SGPR a
+// VALU instruction wrote needs 5 wait states in between (gfx9 hazard), and
+// the compiler does not insert them ahead of inline asm: when it reloads a
+// spilled base with v_readlane right before the load, the load would read
+// a stale base.  The s_nop 4 provides them whatever precedes the load.
 __device__ __forceinline__ void dma16_so(const void* base, uint32_t voff, uint32_t lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "{m0}"(m0)
+               : "memory");
 }
 
 // Load slot plan: slot j of this wave is load k = j * NW + wave of every
@@ -310,6 +320,14 @@ __global__ void __launch_bounds__(512) span_scan_kernel(
   // only when lam would fall below -kLamMin, which bounds every factor below
   // by 2^kLamMin (acc and the weighted x stay far inside float32 and bfloat16).
   constexpr float kLamMin = 64.f;
+  // this wave's decay tables, per head: XW[j] = 2^(cs_e - cs_j) dt_j and
+  // YS[i] = 2^(cs_i - prev) for the block's 32 steps, then F[j] =
+  // 2^(cs_15 - cs_j) dt_j (j < 16) and E[i] = 2^(cs_i - cs_15) (i >= 16), the
+  // two factors of the off-diagonal G^T tile's weights.  Every exponent is a
+  // difference of cumulative sums in time order, never positive, so no
+  // factor overflows.  Formed by the wave's lanes once per block (two
+  // exponentials each) instead of by every lane for its own steps.
+  float* const tab = (float*)(smem + C::NBUF * C::BUF) + w * (HPW * 96);
   float prev[HPW], lam[HPW];
 #pragma unroll
   for (int k = 0; k < HPW; ++k) prev[k] = lam[k] = 0.f;
@@ -391,23 +409,38 @@ __global__ void __launch_bounds__(512) span_scan_kernel(
       const f32x4 dta = *(const f32x4*)(dt + 4 * q), dtb = *(const f32x4*)(dt + 16 + 4 * q);
       const float cse = cs[31];
       const float ci0 = cs[L16], ci1 = cs[16 + L16];
+      float* const tb = tab + k * 96;
+      {
+        const int li = lane & 31;
+        const bool lo = lane < 32, mid = !lo && lane < 48;
+        const float c15 = cs[15], csl = cs[li];
+        const float a0 = lo ? cse - csl : (mid ? c15 - csl : csl - c15);
+        const float m0 = (lo || mid) ? dt[li] : 1.f;
+        tb[lo ? li : 64 + li] = fast_exp2(a0) * m0;
+        const float ys = fast_exp2(csl - prev[k]);
+        if (lo) tb[32 + li] = ys;
+      }
+      const f32x4 xw0 = *(const f32x4*)(tb + 4 * q), xw1 = *(const f32x4*)(tb + 16 + 4 * q);
+      const f32x4 f01 = *(const f32x4*)(tb + 64 + 4 * q);
+      const float ys0 = tb[32 + L16], ys1 = tb[48 + L16], e01 = tb[80 + L16];
       // carried-state part: h = 2^lam acc, decayed from the step before the block
-      Y[k][0] *= fast_exp2(ci0 - prev[k] + lam[k]);
-      Y[k][1] *= fast_exp2(ci1 - prev[k] + lam[k]);
-      // weights G^T[j, i] 2^(cs_i - lw_j), lw_j = cs_j - log2 dt_j (dt_j = 0
-      // gives +inf and weight 0), causal mask, D on the diagonal; this lane's
-      // steps are j = 4 q + e (i-tile 0 and 1) and 16 + 4 q + e (i-tile 1)
+      const float sl = fast_exp2(lam[k]);
+      Y[k][0] *= ys0 * sl;
+      Y[k][1] *= ys1 * sl;
+      // weights G^T[j, i] 2^(cs_i - cs_j) dt_j, causal mask, D on the
+      // diagonal; this lane's steps are j = 4 q + e (i-tiles 0 and 1) and
+      // 16 + 4 q + e (i-tile 1).  Inside the diagonal tiles the exponent is
+      // formed per element (never positive where the mask keeps it); the
+      // off-diagonal tile takes E[i] F[j].
       f32x4 w0a, w1a, w1b;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = 4 * q + e;
-        const float la = csa[e] - __builtin_amdgcn_logf(dta[e]);
-        const float lb = csb[e] - __builtin_amdgcn_logf(dtb[e]);
-        float v0 = j <= L16 ? G00[e] * fast_exp2(ci0 - la) : 0.f;
+        float v0 = j <= L16 ? G00[e] * (fast_exp2(ci0 - csa[e]) * dta[e]) : 0.f;
         if (j == L16) v0 += Dh[k];
         w0a[e] = v0;
-        w1a[e] = G01[e] * fast_exp2(ci1 - la);
-        float v1 = j <= L16 ? G11[e] * fast_exp2(ci1 - lb) : 0.f;
+        w1a[e] = G01[e] * (e01 * f01[e]);
+        float v1 = j <= L16 ? G11[e] * (fast_exp2(ci1 - csb[e]) * dtb[e]) : 0.f;
         if (j == L16) v1 += Dh[k];
         w1b[e] = v1;
       }
@@ -438,11 +471,12 @@ __global__ void __launch_bounds__(512) span_scan_kernel(
         lnew = 0.f;
       }
       lam[k] = lnew;
+      const float sx = fast_exp2(-lnew);
       f32x4 xa, xb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        xa[e] = bf2f(xop[e]) * (fast_exp2(cse - csa[e] - lnew) * dta[e]);
-        xb[e] = bf2f(xop[4 + e]) * (fast_exp2(cse - csb[e] - lnew) * dtb[e]);
+        xa[e] = bf2f(xop[e]) * (xw0[e] * sx);
+        xb[e] = bf2f(xop[4 + e]) * (xw1[e] * sx);
       }
       wx[k] = to_bf8(xa, xb);
       prev[k] = jb == C::BPC - 1 ? 0.f : cse;
