@@ -78,6 +78,34 @@ def test_chunk_cumsum(m2, w):
     np.testing.assert_array_equal(f64(dtt), odt)
 
 
+# Long sequences of many chunks for chunk_cumsum, with a ragged last chunk
+# and a last head tile of 4 heads, through the scalar (H % 8 != 0, bfloat16)
+# and the vector (float32) dt loads.
+CUMSUM_WIDE = [
+    _custom(name="cumsum_long_bf16_H36", batch=1, seqlen=1022 * 64 + 17, nheads=36, headdim=16,
+            dstate=16, ngroups=1, chunk_size=64, seed=29),
+    _custom(name="cumsum_long_f32_H12", batch=2, seqlen=300 * 32 + 5, nheads=12, headdim=16,
+            dstate=16, ngroups=1, chunk_size=32, dtype="f32", seed=30),
+]
+
+
+@pytest.mark.parametrize("w", CUMSUM_WIDE, ids=lambda w: w.name)
+def test_chunk_cumsum_long_ragged(m2, w):
+    say(f"[cumsum wide] {w}")
+    inp = ssd_inputs.make_inputs(w)
+    g = to_gpu(inp)
+    dims = m2.dims_of(g["x"], g["B"], w.chunk_size)
+    cs, dtt, _ = m2.stage_buffers(dims, g["x"].device)
+    m2.mamba2_chunk_cumsum(dims, g["dt"], g["A"], cs, dtt)
+    torch.cuda.synchronize()
+    ocs, odt = oracle.chunk_cumsum(f32(inp["dt"]), f32(inp["A"]), w.chunk_size)
+    got = f64(cs)
+    rel = np.abs(got - ocs) / np.where(ocs == 0, 1.0, np.abs(ocs))
+    assert np.all(got[ocs == 0] == 0)
+    assert rel.max() <= CUMSUM_TOL, rel.max()
+    np.testing.assert_array_equal(f64(dtt), odt)
+
+
 @pytest.mark.parametrize("w", _all_small(), ids=lambda w: w.name)
 def test_stages_and_forward(m2, w):
     """Chained stages and the whole forward against the oracle's definitions:
