@@ -693,6 +693,10 @@ def backward_model(w):
     th = B * nc * H * (N // 64) * Q * 4
     fwd = stage_model(w)
     m = {k: fwd[k] for k in ("chunk_cumsum", "chunk_state", "state_passing")}
+    if span_plan(w):
+        # the chunk-start states recomputed over spans, as the forward does:
+        # the profile's two stages are span_end and the jump plus the replay
+        m["chunk_state"], m["state_passing"] = fwd["span_end"], fwd["span_pass"]
     m["adjoint_state"] = dict(flops=2 * N * P * tok * H, bytes=x + bc + 2 * csb + st)
     m["reverse_pass"] = dict(flops=2 * st // 4 + 2 * st // 4,
                              bytes=st + hs + B * H * nc * 4 + 2 * fin + hs)

@@ -420,9 +420,25 @@ int enqueue_backward(const m2::Dims& d, const void* x, const void* dt, const flo
   mark();
   e = e == hipSuccess ? m2::launch_chunk_cumsum(d, dt, A, dA_cs, dt_T, s) : e;
   mark();
-  e = e == hipSuccess ? m2::launch_chunk_state_grouped(d, x, B, dA_cs, dt_T, st, s) : e;
-  mark();
-  e = e == hipSuccess ? m2::launch_state_passing_bf16(d, st, dA_cs, init_state, hst, fin, s) : e;
+  // the forward's bf16 chunk-start states: over spans of chunks where the
+  // forward takes that path (the span states and decays borrow the float32
+  // state slot, which the adjoint states fill afterwards), else chunk_state
+  // then state_passing; the profile's two stages are span_end and the jump
+  // plus the replay there
+  const int K = m2::span_chunks(d);
+  if (K) {
+    hipEvent_t mid = (ev && e == hipSuccess) ? ev[stage] : nullptr;
+    float* sdec = (float*)((char*)st + round256(m2::span_states_bytes(d, K)));
+    e = e == hipSuccess ? m2::launch_fwd_pass_state_span(d, K, x, B, dA_cs, dt_T, init_state, st,
+                                                         sdec, hst, fin, s, mid, true)
+                        : e;
+    ++stage;
+  } else {
+    e = e == hipSuccess ? m2::launch_chunk_state_grouped(d, x, B, dA_cs, dt_T, st, s) : e;
+    mark();
+    e = e == hipSuccess ? m2::launch_state_passing_bf16(d, st, dA_cs, init_state, hst, fin, s)
+                        : e;
+  }
   mark();
   e = e == hipSuccess ? m2::launch_chunk_state_adjoint(d, dy, C, dA_cs, dt_T, st, s) : e;
   mark();

@@ -122,6 +122,20 @@ def test_backward_multichunk_long(m2):
     say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
+def test_backward_recompute_over_spans(m2):
+    """A shape whose forward runs fwd_pass_state over spans of chunks (the
+    span-end states, the jump across spans and the replay): the backward
+    recomputes its chunk-start states the same way."""
+    from test_gpu_span_state import span_chunks
+    w = _w("bwd_span_L8192_N128", 8192, 32, 128, 2, 128, seed=74)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert span_chunks(w, cus) > 0
+    say(f"backward {w.name}")
+    got, ref = _run(m2, w)
+    errs = _compare(got, ref)
+    say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
 def test_backward_writes_only_its_outputs(m2):
     w = SHAPES[4]
     inp = ssd_inputs.make_inputs(w)
