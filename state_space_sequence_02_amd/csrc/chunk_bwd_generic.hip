@@ -502,10 +502,14 @@ __device__ __forceinline__ void mw_tile(float (*mw)[kT + 1], int64_t i0, int64_t
 }
 
 // dC (DB = false) or dB (DB = true) of one (batch, chunk, group) row tile and
-// state-column tile, summed over the group's heads:
+// up to kNG state-column tiles, summed over the group's heads:
 //   dC_i = sum_h [sum_{j<=i} (M o W)_ij B_j + 2^cs_i dy_i h]
 //   dB_j = sum_h [sum_{i>=j} (M o W)_ij C_i + 2^(cl - cs_j) dt_j x_j g]
-// Grid: (q tiles x n tiles, nc, B G).
+// Per head the (M o W) tiles that meet the row tile are formed once into LDS
+// and used for every column tile (kNG accumulator tiles per thread).
+// Grid: (q tiles x column-tile groups, nc, B G).
+constexpr int kNG = 2;
+
 template <typename T, bool DB>
 __global__ void __launch_bounds__(256) gb_dbdc_kernel(
     const T* __restrict__ x, const T* __restrict__ dy, const T* __restrict__ Bm,
@@ -514,17 +518,21 @@ __global__ void __launch_bounds__(256) gb_dbdc_kernel(
     int64_t P, int64_t N, int64_t nc, int Q, int nNt, int nQt) {
   __shared__ Stage s;
   __shared__ float cs[256], dts[256];
-  __shared__ float mw[kT][kT + 1];
+  __shared__ float mw[4][kT][kT + 1];  // Q <= 256: at most four tiles meet a row tile
+  const int nNg = (nNt + kNG - 1) / kNG;
   const int64_t b = blockIdx.z / G, g = blockIdx.z % G, c = blockIdx.y;
-  const int64_t r0 = (int64_t)(blockIdx.x / nNt) * kT, n0 = (int64_t)(blockIdx.x % nNt) * kT;
-  const int rt = blockIdx.x / nNt;
+  const int rt = blockIdx.x / nNg, ng = blockIdx.x % nNg;
+  const int64_t r0 = (int64_t)rt * kT;
+  const int nt0 = ng * kNG;
   const int64_t t0 = c * Q, rem = L - t0;
   const int Lc = (int)(rem < Q ? rem : Q);
   const int64_t HG = H / G, HP = H * P;
   // the other operand of the in-chunk term: B rows for dC, C rows for dB
   const T* ob = (DB ? Cm : Bm) + ((b * L + t0) * G + g) * N;
-  float acc[4][4];
-  zero(acc);
+  const int lo = DB ? rt : 0, hi = DB ? nQt - 1 : rt;
+  float acc[kNG][4][4];
+#pragma unroll
+  for (int u = 0; u < kNG; ++u) zero(acc[u]);
   if (r0 < Lc) {
     for (int64_t hh = 0; hh < HG; ++hh) {
       const int64_t h = g * HG + hh;
@@ -535,46 +543,59 @@ __global__ void __launch_bounds__(256) gb_dbdc_kernel(
       const T* dyb = dy + ((b * L + t0) * H + h) * P;
       const T* xb = x + ((b * L + t0) * H + h) * P;
       const float* sm = st_ + ((b * nc + c) * H + h) * P * N;  // h_c (dC) or g_c (dB)
-      // state term over p
-      mm<true, false>(
-          acc, 0, (int)P,
-          [&](int r, int p) {
-            const int64_t i = r0 + r;
-            if (i >= Lc) return 0.f;
-            return DB ? fast_exp2(cl - cs[i]) * dts[i] * ld(xb + i * HP + p)
-                      : fast_exp2(cs[i]) * ld(dyb + i * HP + p);
-          },
-          [&](int r, int p) { return n0 + r < N ? sm[(int64_t)p * N + n0 + r] : 0.f; }, s);
-      // in-chunk term, tile by tile of the other index
-      const int lo = DB ? rt : 0, hi = DB ? nQt - 1 : rt;
+      // this head's (M o W) tiles against the row tile
       for (int ot = lo; ot <= hi; ++ot) {
         const int64_t o0 = (int64_t)ot * kT;
         if (o0 >= Lc) break;
-        __syncthreads();
         if (DB)
-          mw_tile(mw, o0, r0, Lc, dyb, xb, HP, P, cs, dts, s);  // rows i, columns j
+          mw_tile(mw[ot - lo], o0, r0, Lc, dyb, xb, HP, P, cs, dts, s);  // rows i, columns j
         else
-          mw_tile(mw, r0, o0, Lc, dyb, xb, HP, P, cs, dts, s);
-        __syncthreads();
-        mm<false, false>(
-            acc, 0, kT,
-            [&](int r, int q) { return DB ? mw[q][r] : mw[r][q]; },
-            [&](int r, int q) {
-              const int64_t t = o0 + q;
-              return (t < Lc && n0 + r < N) ? ld(ob + t * G * N + n0 + r) : 0.f;
+          mw_tile(mw[ot - lo], r0, o0, Lc, dyb, xb, HP, P, cs, dts, s);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kNG; ++u) {
+        if (nt0 + u >= nNt) break;  // uniform
+        const int64_t n0 = (int64_t)(nt0 + u) * kT;
+        // state term over p
+        mm<true, false>(
+            acc[u], 0, (int)P,
+            [&](int r, int p) {
+              const int64_t i = r0 + r;
+              if (i >= Lc) return 0.f;
+              return DB ? fast_exp2(cl - cs[i]) * dts[i] * ld(xb + i * HP + p)
+                        : fast_exp2(cs[i]) * ld(dyb + i * HP + p);
             },
-            s);
+            [&](int r, int p) { return n0 + r < N ? sm[(int64_t)p * N + n0 + r] : 0.f; }, s);
+        // in-chunk term, tile by tile of the other index
+        for (int ot = lo; ot <= hi; ++ot) {
+          const int64_t o0 = (int64_t)ot * kT;
+          if (o0 >= Lc) break;
+          const float(*m)[kT + 1] = mw[ot - lo];
+          mm<false, false>(
+              acc[u], 0, kT, [&](int r, int q) { return DB ? m[q][r] : m[r][q]; },
+              [&](int r, int q) {
+                const int64_t t = o0 + q;
+                return (t < Lc && n0 + r < N) ? ld(ob + t * G * N + n0 + r) : 0.f;
+              },
+              s);
+        }
       }
     }
   }
   const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int u = 0; u < kNG; ++u) {
+    if (nt0 + u >= nNt) break;
+    const int64_t n0 = (int64_t)(nt0 + u) * kT;
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const int64_t r = r0 + 4 * tr + a, n = n0 + 4 * tc + bb;
-      if (r < Lc && n < N) st(out + ((b * L + t0 + r) * G + g) * N + n, acc[a][bb]);
-    }
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int64_t r = r0 + 4 * tr + a, n = n0 + 4 * tc + bb;
+        if (r < Lc && n < N) st(out + ((b * L + t0 + r) * G + g) * N + n, acc[u][a][bb]);
+      }
+  }
 }
 
 template <typename T>
@@ -607,9 +628,10 @@ hipError_t launch_generic(const Dims& d, const void* x, const void* dy, const vo
   gb_dq_kernel<T><<<dim3(nc, BH), 256, 0, s>>>(
       xt, dyt, w.cb, w.vg, w.thp, w.xup, w.ghp, dA_cs, dt_T, A, (T*)ddt, w.dA_part, w.dD_part,
       d.L, d.H, d.G, d.P, d.nc, Q, nPt, nQt, ngh);
-  gb_dbdc_kernel<T, false><<<dim3(nQt * nNt, nc, BG), 256, 0, s>>>(
+  const unsigned nNg = (unsigned)((nNt + kNG - 1) / kNG);
+  gb_dbdc_kernel<T, false><<<dim3(nQt * nNg, nc, BG), 256, 0, s>>>(
       xt, dyt, Bt, Ct, hs, dA_cs, dt_T, (T*)dC, d.L, d.H, d.G, d.P, d.N, d.nc, Q, nNt, nQt);
-  gb_dbdc_kernel<T, true><<<dim3(nQt * nNt, nc, BG), 256, 0, s>>>(
+  gb_dbdc_kernel<T, true><<<dim3(nQt * nNg, nc, BG), 256, 0, s>>>(
       xt, dyt, Bt, Ct, E, dA_cs, dt_T, (T*)dB, d.L, d.H, d.G, d.P, d.N, d.nc, Q, nNt, nQt);
   return hipGetLastError();
 }
