@@ -551,11 +551,12 @@ hipError_t launch_ss_qn(const Dims& d, int K, const void* x, const void* B, cons
 }  // namespace
 
 int span_scan_heads(const Dims& d, int K) {
-  // State size 256 is not taken: with one head per wave every wave reads the
+  // State size 256 is not taken.  With one head per wave every wave reads the
   // block's whole B and C rows for a single head (about 6 KB of LDS reads per
   // token and head against 2.4 KB for the replay plus the grouped chunk_scan),
   // and it measured slower than those two kernels (400 us against 354 us at
-  // L = 64K); two heads per wave do not fit the registers there.
+  // L = 64K).  Two heads per wave (four per workgroup) fill all 256 registers
+  // and measured slower still (442 us against 355 us).
   if (!(d.bf16 && d.P == 64 && (d.N == 64 || d.N == 128) &&
         (d.Q == 64 || d.Q == 128 || d.Q == 256) && K > 0))
     return 0;
