@@ -521,17 +521,34 @@ __device__ __forceinline__ void issue_rows_loads(uint32_t buf, const bf16* __res
 template <int Q>
 struct WsLds {
   static constexpr int BUF = 2 * Q * 128 + 2 * Q * 4;  // dY, x rows; cs, dt
-  static constexpr int RP = 2 * BUF;                    // rectangle-sum parts, 2 x [NW][Q]
-  static constexpr int BYTES = RP + 2 * BwdCfg<Q>::NW * Q * 4;
+  static constexpr int RP = 2 * BUF;                    // column-sum parts, 2 x [NW][Q]
+  static constexpr int RS = RP + 2 * BwdCfg<Q>::NW * Q * 4;  // row sums, 2 x [Q]
+  static constexpr int BYTES = RS + 2 * Q * 4;
   static_assert(2 * Q * 128 <= 2 * BUF, "setup slices of C and B fit in the head buffers");
+  static_assert(Q <= 256, "one wave forms the prefix over the chunk");
 };
+
+// Inclusive prefix sum over the 64 lanes of a wave: inside each 16-lane row,
+// then each row total carried into the rows above it (row_bcast 15 into rows
+// 1 and 3, row_bcast 31 into rows 2 and 3).
+__device__ __forceinline__ float wave_scan64(float v) {
+  v = row_scan16(v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));
+  return v;
+}
 
 // Per head also the rectangle sums of the log-decay gradient,
 //     R_k = sum_{i >= k > j} T_ij,   T_ij = (M o CB)_ij dt_j (dy_i . x_j),
-// from the same W tiles: the wave owns whole row strips, so it forms the
-// prefix sums of T along each of its rows (DPP scans inside a tile, a carry
-// across the strip) and adds, for every column k, the prefixes of its rows
-// i >= k; the per-wave column parts are summed after the head.
+// from the same W tiles.  Going from k to k + 1 the rectangle gains column
+// k below the diagonal and loses row k left of it, so
+//     R_k = sum_{m < k} (colsum_m - rowsum_m),
+//     colsum_m = sum_{i > m} T_im,   rowsum_m = sum_{j < m} T_mj.
+// Per tile each lane adds its T values into running row sums (one per row
+// it holds, over the strip) and a column sum (over its rows, then across the
+// four lane groups); after the head the row sums are reduced across their 16
+// lanes, and one wave forms the prefix over the chunk from the per-wave
+// column parts and the row sums.
 template <int Q>
 __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
     const bf16* __restrict__ x, const bf16* __restrict__ dy, const bf16* __restrict__ Bm,
@@ -554,6 +571,7 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
   const int64_t valid = (int64_t)L - tok0;
   const uint32_t base = lds_addr(smem);
   float* rp = (float*)(smem + S::RP);
+  float* rs = (float*)(smem + S::RS);
 
   // ---- C B^T of the group on this wave's triangle tiles (float32)
   f32x4 cb[SLOTS];
@@ -591,17 +609,32 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
     issue_rows_loads<Q>(base + slot * S::BUF, dy + xrow0, x + xrow0, (int64_t)H * P, valid,
                         dA_cs + cb0, dt_T + cb0);
   };
-  // R of head h from the parts in rp[buf], which are zeroed for reuse
-  auto finish_rect = [&](int h, int buf) {
+  // R of head h from the column parts in rp[buf] (zeroed for reuse) and the
+  // row sums in rs[buf], by wave `fw`: lane l takes m = 4 l .. 4 l + 3
+  auto finish_rect = [&](int h, int buf, int fw) {
+    if (w != fw) return;
     float* part = rp + buf * NW * Q;
-    float* out = rsum + (((int64_t)b * H + h) * nc + c) * Q;
-    for (int k = threadIdx.x; k < Q; k += NT) {
+    const float* rows = rs + buf * Q;
+    float d[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * lane + e;
       float v = 0.f;
-      for (int i = 0; i < NW; ++i) {
-        v += part[i * Q + k];
-        part[i * Q + k] = 0.f;
+      if (m < Q) {
+        for (int i = 0; i < NW; ++i) {
+          v += part[i * Q + m];
+          part[i * Q + m] = 0.f;
+        }
+        v -= rows[m];
       }
-      out[k] = v;
+      d[e] = v;
+    }
+    const float tot = ((d[0] + d[1]) + d[2]) + d[3];
+    const float pre = wave_scan64(tot) - tot;  // sum over the lanes below
+    float* out = rsum + (((int64_t)b * H + h) * nc + c) * Q;
+    if (4 * lane < Q) {
+      const float r1 = pre + d[0], r2 = r1 + d[1], r3 = r2 + d[2];
+      *(f32x4*)(out + 4 * lane) = f32x4{pre, r1, r2, r3};
     }
   };
 
@@ -615,7 +648,7 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
     __syncthreads();                // ... for every wave; the other buffer is free
     // (before the next head's loads are issued: anything the compiler waits
     // for here would otherwise wait for them too)
-    if (hh > 0) finish_rect(g * HG + hh - 1, (hh - 1) & 1);
+    if (hh > 0) finish_rect(g * HG + hh - 1, (hh - 1) & 1, (hh - 1) % NW);
     if (hh + 1 < HG) issue(g * HG + hh + 1, (hh + 1) & 1);
     const unsigned char* cur = smem + (hh & 1) * S::BUF;
     const bf16* Ys = (const bf16*)cur;
@@ -624,14 +657,21 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
     const float* dts = css + Q;
     float* part = rp + (hh & 1) * NW * Q + w * Q;
     const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
-    float carry[4] = {0.f, 0.f, 0.f, 0.f};
+    float* rows = rs + (hh & 1) * Q;
+    // running row sums of the current strip: at its end, across the 16 lanes
+    // of each row into rows[]
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+    auto flush_rows = [&](int ti) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float t = row_scan16(rsum[r]);
+        if (L16 == 15) rows[ti * 16 + 4 * grp + r] = t;
+        rsum[r] = 0.f;
+      }
+    };
 #pragma unroll
     for (int k = 0; k < SLOTS; ++k) {
       const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
-      if (k == w + 1) {  // second row strip
-#pragma unroll
-        for (int r = 0; r < 4; ++r) carry[r] = 0.f;
-      }
       f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -650,19 +690,19 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
         const float wm = e * a4[r];
         ws[k][r] += wm;
         const float t = (i > j) ? cb[k][r] * wm : 0.f;
-        const float inc = row_scan16(t);
-        const float pm = carry[r] + row_prev(inc);  // sum_{j' < j} T[i][j'] along the row
-        carry[r] += __shfl(inc, 15, 16);
-        if (j <= i) col += pm;
+        rsum[r] += t;
+        col += t;
       }
       col += __shfl_xor(col, 16, 64);
       col += __shfl_xor(col, 32, 64);
       if (grp == 0) part[j] += col;
+      if (k == w) flush_rows(w);  // end of the first strip (wave-uniform)
       __builtin_amdgcn_sched_barrier(0);
     }
+    flush_rows(QT - 1 - w);
   }
   __syncthreads();
-  finish_rect(g * HG + HG - 1, (HG - 1) & 1);
+  finish_rect(g * HG + HG - 1, (HG - 1) & 1, (HG - 1) % NW);
 
   const int L16 = lane & 15, grp = lane >> 4;
   bf16* out = wsum + (((int64_t)b * nc + c) * G + g) * (int64_t)(K::NTILE * 256);
@@ -860,10 +900,8 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
       float* tho = th + ((((int64_t)b * nc + c) * H + h) * nT + nt) * Q + R[s] * 16 + 4 * grp;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float v = thr[r];
-#pragma unroll
-        for (int mm = 1; mm < 16; mm <<= 1) v += __shfl_xor(v, mm, 64);
-        if (L16 == 0) tho[r] = v;
+        const float v = row_scan16(thr[r]);  // the row's total in its last lane
+        if (L16 == 15) tho[r] = v;
       }
     }
   }
