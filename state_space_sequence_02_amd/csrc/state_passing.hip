@@ -121,38 +121,44 @@ __global__ void __launch_bounds__(kThreads) state_passing_reverse_kernel(
   f32x4 run = f32x4{0.f, 0.f, 0.f, 0.f};
   if (dfinal && live) run = dfinal[bh * PNv + g];
 
-  // slot k of a ring holds chunk nc-1-(c0+k): its E and its start state
+  // slot k of a ring holds chunk nc-1-(c0+k): its E, its start state and its
+  // total log decay.  Every slot is reloaded unconditionally (chunks past the
+  // first clamped to chunk 0, loaded and never used), so no value in the ring
+  // is a merge of a fresh load with an old one: the compiler then never has
+  // to wait for the load it just issued, which would also wait for every
+  // older load of the ring.
   f32x4 eb[kDepth];
   bf16x4 hb[kDepth];
+  float lb[kDepth];
 #pragma unroll
   for (int k = 0; k < kDepth; ++k) {
-    const int c = nc - 1 - k;
-    if (c >= 0) {
-      eb[k] = __builtin_nontemporal_load(E + base + (int64_t)c * chunk_stride);
-      hb[k] = hst[base + (int64_t)c * chunk_stride];
-    }
+    const int c = max(nc - 1 - k, 0);
+    eb[k] = __builtin_nontemporal_load(E + base + (int64_t)c * chunk_stride);
+    hb[k] = hst[base + (int64_t)c * chunk_stride];
+    lb[k] = cs_last[(int64_t)c * Q];
   }
   for (int c0 = 0; c0 < nc; c0 += kDepth) {
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {
       const int c = nc - 1 - (c0 + k);
+      const f32x4 cur = eb[k];
+      const bf16x4 hcur = hb[k];
+      const float lc = lb[k];
+      const int cn = max(c - kDepth, 0);  // chunk this slot holds next
+      eb[k] = __builtin_nontemporal_load(E + base + (int64_t)cn * chunk_stride);
+      hb[k] = hst[base + (int64_t)cn * chunk_stride];
+      lb[k] = cs_last[(int64_t)cn * Q];
       if (c >= 0) {
-        const f32x4 cur = eb[k];
         f32x4 hc;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hc[e] = bf2f(hb[k][e]);
-        const int cn = c - kDepth;  // chunk this slot holds next
-        if (cn >= 0) {
-          eb[k] = __builtin_nontemporal_load(E + base + (int64_t)cn * chunk_stride);
-          hb[k] = hst[base + (int64_t)cn * chunk_stride];
-        }
+        for (int e = 0; e < 4; ++e) hc[e] = bf2f(hcur[e]);
         if (live) {
           bf16x4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = f2bf(run[e]);
           gst[base + (int64_t)c * chunk_stride] = o;
         }
-        const float decay = exp2f(cs_last[(int64_t)c * Q]);
+        const float decay = exp2f(lc);
         float part = live ? run[0] * hc[0] + run[1] * hc[1] + run[2] * hc[2] + run[3] * hc[3] : 0.f;
         part = wave_total_in_lane63(part);
         if ((threadIdx.x & 63) == 63) dot_out[(int64_t)c * wph] = decay * part;
