@@ -472,12 +472,22 @@ KERNEL_SOURCES = {
 }
 
 
-def sources_digest(stage):
+def stage_sources(stage, direction="forward", workload_name=None):
+    """The source files of `stage`'s kernel.  The backward's recompute stages
+    (chunk_state, state_passing) run the forward's span kernels where the
+    workload takes the span path."""
+    if (direction == "backward" and stage in ("chunk_state", "state_passing")
+            and workload_name is not None and span_plan(workload(workload_name))):
+        return KERNEL_SOURCES["span_end"]
+    return KERNEL_SOURCES[stage]
+
+
+def sources_digest(stage, direction="forward", workload_name=None):
     """sha256 over the files that define `stage`'s kernel (names and bytes)."""
     import hashlib
     d = os.path.join(ROOT, "state_space_sequence_02_amd", "csrc")
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[stage]:
+    for f in stage_sources(stage, direction, workload_name):
         h.update(f.encode())
         with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())
@@ -494,7 +504,7 @@ def profiled_traffic(workload, stage, direction="forward"):
         return None
     text = open(path).read()
     m = re.search(rf"sources-sha256 {stage}: ([0-9a-f]{{64}})", text)
-    if not m or m.group(1) != sources_digest(stage):
+    if not m or m.group(1) != sources_digest(stage, direction, workload):
         return None
     for line in text.splitlines():
         cells = [c.strip() for c in line.strip().strip("|").split("|")]

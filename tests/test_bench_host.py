@@ -100,6 +100,25 @@ def test_committed_profiles_parse():
                 assert 0.9 < t / bench.stage_model(w)[st]["bytes"] < 1.6, (name, st, t)
 
 
+def test_committed_backward_profile_parses():
+    """The backward summary yields every stage's traffic while its sources
+    match; its recompute stages are the forward's span kernels at this shape,
+    so their digests cover state_span.hip."""
+    name = "long_L64k_N256"
+    w = bench.workload(name)
+    text = open(os.path.join(ROOT, "profiles", f"ssd_backward_{name}.md")).read()
+    assert bench.stage_sources("chunk_state", "backward", name) == bench.KERNEL_SOURCES["span_end"]
+    assert bench.stage_sources("chunk_state") == bench.KERNEL_SOURCES["chunk_state"]
+    model = bench.backward_model(w)
+    for st in ("chunk_cumsum", "chunk_state", "state_passing", "adjoint_state", "reverse_pass",
+               "dB_dC", "dx"):
+        t = bench.profiled_traffic(name, st, "backward")
+        current = f"sources-sha256 {st}: {bench.sources_digest(st, 'backward', name)}" in text
+        assert (t is not None) == current, st
+        if t is not None:
+            assert 0.9 < t / model[st]["bytes"] < 1.6, (st, t)
+
+
 def test_workload_names():
     w = bench.workload("sweep_L16k_N64")
     assert (w.seqlen, w.dstate, w.nheads, w.headdim, w.chunk_size) == (16384, 64, 32, 64, 256)
