@@ -4,13 +4,13 @@
 // inclusive cumsum along the chunk, times LOG2E; section 3: the cumsum and dt
 // stored so later stages read them contiguously).
 //
-// One workgroup per (chunk, head tile, batch); thread i owns time step i of
-// the chunk and reads its head tile's dt values with 16-byte loads (they are
-// contiguous in [B, L, H]).  The sum is a tree: a log-depth scan inside each
-// 64-lane wavefront on the VALU's cross-lane (DPP) paths, then the wave
-// totals added through LDS.  Every partial sum is of same-sign terms
-// (A <= 0, dt >= 0), so its relative error grows with the tree depth (at most
-// 9 roundings for Q = 256) rather than with Q.
+// One wavefront per (chunk, head tile, batch); lane l owns time steps
+// 4 l .. 4 l + 3 of the chunk and reads its head tile's dt values with 16-byte
+// loads (they are contiguous in [B, L, H]).  The sum is a tree: the lane's
+// four steps in order, then a log-depth scan of the lane totals across the
+// wavefront on the VALU's cross-lane (DPP) paths.  Every partial sum is of
+// same-sign terms (A <= 0, dt >= 0), so its relative error grows with the
+// tree depth (at most 10 roundings for Q = 256) rather than with Q.
 //
 // Outputs are time-contiguous [B, H, nc, Q] float32: dA_cs (log2 units) and
 // dt_T (dt transposed, 0 past the end of the sequence).
@@ -21,7 +21,7 @@ namespace m2 {
 
 namespace {
 
-constexpr int kHeadTile = 8;  // heads per workgroup: one 16-byte bf16 dt load per thread
+constexpr int kHeadTile = 8;  // heads per wavefront: one 16-byte bf16 dt load per time step
 
 template <typename T>
 __device__ __forceinline__ float load_f32(const T* p);
@@ -63,68 +63,76 @@ __device__ __forceinline__ float wave_scan(float v) {
   return v;
 }
 
+// One wavefront per (chunk, head tile, batch), four per workgroup; lane l
+// owns time steps 4 l .. 4 l + 3 of the chunk (Q <= 256) for the tile's
+// heads.  Per head: the lane's four steps summed in order, the lane totals
+// scanned across the wavefront, and the lane's exclusive prefix (the
+// inclusive scan of the lane below, moved up one lane) added to its four
+// partial sums; outputs leave as one 16-byte store per head and array.
 template <typename T>
 __global__ void __launch_bounds__(256) chunk_cumsum_kernel(const T* __restrict__ dt,
                                                            const float* __restrict__ A,
                                                            float* __restrict__ dA_cs,
                                                            float* __restrict__ dt_T, int L, int H,
-                                                           int Q, int nc) {
-  __shared__ float wave_tot[kHeadTile][4];
+                                                           int Q, int nc, int ntile) {
   const int c = blockIdx.x;
-  const int h0 = blockIdx.y * kHeadTile;
+  const int tile = blockIdx.y * 4 + wave_id();
   const int b = blockIdx.z;
-  const int i = threadIdx.x;  // time step in the chunk
-  const int lane = lane_id();
-  const int w = wave_id();
-  const int nwaves = (blockDim.x + 63) >> 6;
-  const int t = c * Q + i;
+  if (tile >= ntile) return;  // whole wavefront
+  const int h0 = tile * kHeadTile;
   const int nh = min(kHeadTile, H - h0);
+  const int lane = lane_id();
+  const int i0 = 4 * lane;  // this lane's first step in the chunk
 
-  float v[kHeadTile];
-  float dtv[kHeadTile];
+  float dtv[4][kHeadTile];
 #pragma unroll
-  for (int k = 0; k < kHeadTile; ++k) dtv[k] = 0.f;
-  if (i < Q && t < L) {
-    const T* src = dt + ((int64_t)b * L + t) * H + h0;
-    constexpr int VE = Vec16<T>::n;
-    if (H % VE == 0) {  // h0 is a multiple of the head tile (8), so of VE: every vector is aligned
+  for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int k0 = 0; k0 < kHeadTile; k0 += VE) {
-        if (k0 < nh) {
-          const typename Vec16<T>::type u = *(const typename Vec16<T>::type*)(src + k0);
+    for (int k = 0; k < kHeadTile; ++k) dtv[s][k] = 0.f;
+  constexpr int VE = Vec16<T>::n;
 #pragma unroll
-          for (int e = 0; e < VE; ++e) dtv[k0 + e] = (float)u[e];
+  for (int s = 0; s < 4; ++s) {
+    const int64_t t = (int64_t)c * Q + i0 + s;
+    if (i0 + s < Q && t < L) {
+      const T* src = dt + ((int64_t)b * L + t) * H + h0;
+      if (H % VE == 0) {  // h0 is a multiple of the head tile (8), so of VE: every vector is aligned
+#pragma unroll
+        for (int k0 = 0; k0 < kHeadTile; k0 += VE) {
+          if (k0 < nh) {
+            const typename Vec16<T>::type u = *(const typename Vec16<T>::type*)(src + k0);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) dtv[s][k0 + e] = (float)u[e];
+          }
         }
+      } else {
+#pragma unroll
+        for (int k = 0; k < kHeadTile; ++k)
+          if (k < nh) dtv[s][k] = load_f32(src + k);
       }
-    } else {
-#pragma unroll
-      for (int k = 0; k < kHeadTile; ++k)
-        if (k < nh) dtv[k] = load_f32(src + k);
     }
   }
 #pragma unroll
-  for (int k = 0; k < kHeadTile; ++k) v[k] = (k < nh) ? wave_scan(A[h0 + k] * dtv[k]) : 0.f;
-  if (lane == 63) {
+  for (int k = 0; k < kHeadTile; ++k) {
+    if (k < nh) {
+      const float a = A[h0 + k];
+      f32x4 v;
+      v[0] = a * dtv[0][k];
+      v[1] = v[0] + a * dtv[1][k];
+      v[2] = v[1] + a * dtv[2][k];
+      v[3] = v[2] + a * dtv[3][k];
+      const float incl = wave_scan(v[3]);
+      const float pre = __builtin_bit_cast(
+          float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, incl), 0x138, 0xf, 0xf, false));
+      if (i0 < Q) {
+        const int64_t o = (((int64_t)b * H + h0 + k) * nc + c) * Q + i0;
+        f32x4 cs, d;
 #pragma unroll
-    for (int k = 0; k < kHeadTile; ++k) wave_tot[k][w] = v[k];
-  }
-  __syncthreads();
-  if (w > 0) {
-#pragma unroll
-    for (int k = 0; k < kHeadTile; ++k) {
-      float pre = wave_tot[k][0];
-      for (int u = 1; u < w; ++u) pre += wave_tot[k][u];
-      v[k] += pre;
-    }
-  }
-  (void)nwaves;
-  if (i < Q) {
-#pragma unroll
-    for (int k = 0; k < kHeadTile; ++k) {
-      if (k < nh) {
-        const int64_t o = (((int64_t)b * H + h0 + k) * nc + c) * Q + i;
-        dA_cs[o] = v[k] * kLog2e;
-        dt_T[o] = dtv[k];
+        for (int s = 0; s < 4; ++s) {
+          cs[s] = (pre + v[s]) * kLog2e;
+          d[s] = dtv[s][k];
+        }
+        *(f32x4*)(dA_cs + o) = cs;
+        *(f32x4*)(dt_T + o) = d;
       }
     }
   }
@@ -134,14 +142,17 @@ __global__ void __launch_bounds__(256) chunk_cumsum_kernel(const T* __restrict__
 
 hipError_t launch_chunk_cumsum(const Dims& d, const void* dt, const float* A, float* dA_cs,
                                float* dt_T, hipStream_t s) {
-  const int threads = (int)((d.Q + 63) / 64 * 64);
-  dim3 grid((unsigned)d.nc, (unsigned)((d.H + kHeadTile - 1) / kHeadTile), (unsigned)d.B);
+  // one wavefront covers a chunk (4 steps per lane), and the 16-byte stores
+  // need Q % 4 == 0: every supported chunk size (16 .. 256) qualifies
+  if (d.Q > 256 || d.Q % 4 != 0) return hipErrorInvalidValue;
+  const int ntile = (int)((d.H + kHeadTile - 1) / kHeadTile);
+  dim3 grid((unsigned)d.nc, (unsigned)((ntile + 3) / 4), (unsigned)d.B);
   if (d.bf16)
-    chunk_cumsum_kernel<bf16><<<grid, threads, 0, s>>>((const bf16*)dt, A, dA_cs, dt_T, (int)d.L,
-                                                       (int)d.H, (int)d.Q, (int)d.nc);
+    chunk_cumsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)dt, A, dA_cs, dt_T, (int)d.L,
+                                                   (int)d.H, (int)d.Q, (int)d.nc, ntile);
   else
-    chunk_cumsum_kernel<float><<<grid, threads, 0, s>>>((const float*)dt, A, dA_cs, dt_T,
-                                                        (int)d.L, (int)d.H, (int)d.Q, (int)d.nc);
+    chunk_cumsum_kernel<float><<<grid, 256, 0, s>>>((const float*)dt, A, dA_cs, dt_T, (int)d.L,
+                                                    (int)d.H, (int)d.Q, (int)d.nc, ntile);
   return hipGetLastError();
 }
 
