@@ -37,6 +37,12 @@ SHAPES = [
                       ngroups=3, chunk_size=16, dtype="f32", init_state=True, seed=45),
     ssd_inputs.custom(name="dec_f32_N100", batch=1, seqlen=6, nheads=2, headdim=16, dstate=100,
                       ngroups=1, chunk_size=16, dtype="f32", init_state=True, seed=46),
+    # state size 128: two rows per wavefront pass; a row count that leaves
+    # the last wavefront partly idle
+    ssd_inputs.custom(name="dec_bf16_N128_G2", batch=3, seqlen=6, nheads=6, headdim=48,
+                      dstate=128, ngroups=2, chunk_size=64, init_state=True, seed=48),
+    ssd_inputs.custom(name="dec_f32_N128", batch=2, seqlen=6, nheads=4, headdim=16, dstate=128,
+                      ngroups=1, chunk_size=16, dtype="f32", init_state=True, seed=49),
 ]
 
 
@@ -126,16 +132,25 @@ def test_decode_rejects_more_than_one_token(m2):
     assert e.value.status == m2.MAMBA2_ERR_SHAPE
 
 
-def test_decode_serving_batch_sampled(m2):
-    """Batch 64, H = 32, P = 64, N = 256 (a 128 MiB state): one step, checked
-    against the oracle on sampled heads of sampled batch rows."""
-    w = ssd_inputs.custom(name="dec_serving", batch=64, seqlen=1, nheads=32, headdim=64,
-                          dstate=256, ngroups=1, chunk_size=64, init_state=True, seed=47)
+SERVING = [
+    # batch 64, H = 32, P = 64, N = 256: a 128 MiB state, four rows per wavefront
+    ssd_inputs.custom(name="dec_serving", batch=64, seqlen=1, nheads=32, headdim=64,
+                      dstate=256, ngroups=1, chunk_size=64, init_state=True, seed=47),
+    # 2^20 state rows (batch 256, H = 64, P = 64, N = 64): the two-pass form
+    ssd_inputs.custom(name="dec_serving_1M_rows", batch=256, seqlen=1, nheads=64, headdim=64,
+                      dstate=64, ngroups=2, chunk_size=64, init_state=True, seed=50),
+]
+
+
+@pytest.mark.parametrize("w", SERVING, ids=lambda w: w.name)
+def test_decode_serving_batch_sampled(m2, w):
+    """One step at a serving batch size, checked against the oracle on sampled
+    heads (of every group) of sampled batch rows."""
     inp = ssd_inputs.make_inputs(w)
     g = to_gpu(inp)
     y, fin = _decode_all(m2, g, w)
-    heads = [0, 17, 31]
-    for b in (0, 29, 63):
+    heads = [0, w.nheads // 2 + 1, w.nheads - 1]
+    for b in (0, w.batch // 2 - 3, w.batch - 1):
         o = oracle_inputs({k: (None if v is None else v[b:b + 1]) if k != "A" and k != "D" else v
                            for k, v in inp.items()})
         oy, ofin, _ = oracle.ssd_recurrence(o["x"], o["dt"], o["A"], o["B"], o["C"], o["D"],
