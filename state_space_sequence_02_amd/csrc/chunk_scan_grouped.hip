@@ -322,24 +322,40 @@ __global__ void __launch_bounds__(Q * 2) chunk_scan_grouped_kernel(
   for (int a = 0; a <= QT; ++a) Gs[a] = f32x4{0.f, 0.f, 0.f, 0.f};
   bf16x8 C0[NBLK][2], C1[NBLK][2];
   constexpr int ABLK = GBLK > NBLK ? GBLK : NBLK;  // 64-column blocks staged
+  // Each block's C and B rows pass through registers on their way to LDS;
+  // block nb + 1's loads are issued before block nb's MFMAs, so their
+  // latency hides behind them.
+  constexpr int SIT = Q * 8 / nthr;  // 16-byte pieces per thread and block
+  static_assert(Q * 8 % nthr == 0, "staging pieces per thread");
+  bf16x8 sc[SIT], sbv[SIT];
+  auto stage_load = [&](int nb) {
+#pragma unroll
+    for (int it = 0; it < SIT; ++it) {
+      const int idx = tid + it * nthr;
+      const int r = idx >> 3, c8 = (idx & 7) * 8;
+      const int64_t t = tok0 + r;
+      if (t < L) {
+        const int64_t off = (((int64_t)b * L + t) * G + g) * ldn + n0 + nb * 64 + c8;
+        sc[it] = *(const bf16x8*)(Cm + off);
+        if (nb < GBLK) sbv[it] = *(const bf16x8*)(Bm + off);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[it][e] = sbv[it][e] = f2bf(0.f);
+      }
+    }
+  };
+  stage_load(0);
 #pragma unroll
   for (int nb = 0; nb < ABLK; ++nb) {
     lds_barrier();
-    for (int idx = tid; idx < Q * 8; idx += nthr) {
-      const int r = idx >> 3, c8 = (idx & 7) * 8;
-      const int64_t t = tok0 + r;
-      bf16x8 vc, vb;
-      if (t < L) {
-        const int64_t off = (((int64_t)b * L + t) * G + g) * ldn + n0 + nb * 64 + c8;
-        vc = *(const bf16x8*)(Cm + off);
-        if (nb < GBLK) vb = *(const bf16x8*)(Bm + off);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vc[e] = vb[e] = f2bf(0.f);
-      }
-      *(bf16x8*)(Cs + r * SROW + c8) = vc;
-      if (nb < GBLK) *(bf16x8*)(Bs + r * SROW + c8) = vb;
+    for (int it = 0; it < SIT; ++it) {
+      const int idx = tid + it * nthr;
+      const int r = idx >> 3, c8 = (idx & 7) * 8;
+      *(bf16x8*)(Cs + r * SROW + c8) = sc[it];
+      if (nb < GBLK) *(bf16x8*)(Bs + r * SROW + c8) = sbv[it];
     }
+    if (nb + 1 < ABLK) stage_load(nb + 1);
     lds_barrier();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
