@@ -116,23 +116,39 @@ __global__ void __launch_bounds__((SCfg<P, Q, N>::NT), (SCfg<P, Q, N>::WPE)) chu
   const uint32_t sbase = lds_addr(smem);
   load_x<P, Q, N>(sbase, x, dA_cs, dt_T, b, c, h0 + rot, L, H, nc);
 
-  // ---- Phase A: B^T operands of this wave's columns, 64 time steps at a time.
+  // ---- Phase A: B^T operands of this wave's columns, 64 time steps at a time;
+  // the rows pass through registers, block jb + 1's loads issued before
+  // block jb's operand reads so that their latency overlaps.
   bf16x8 Bop[NTW][KS];
+  constexpr int SIT = (64 * (N / 8) + K::NT - 1) / K::NT;  // 16-byte pieces per thread and block
+  bf16x8 sv[SIT];
+  auto stage_load = [&](int jb) {
+#pragma unroll
+    for (int it = 0; it < SIT; ++it) {
+      const int idx = tid + it * K::NT;
+      const int r = idx / (N / 8), c8 = (idx % (N / 8)) * 8;
+      const int64_t t = tok0 + jb * 64 + r;
+      if (idx < 64 * (N / 8) && t < L) {
+        sv[it] = *(const bf16x8*)(Bm + (((int64_t)b * L + t) * G + g) * ldn + ncol0 + c8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[it][e] = f2bf(0.f);
+      }
+    }
+  };
+  stage_load(0);
 #pragma unroll
   for (int jb = 0; jb < Q / 64; ++jb) {
     lds_barrier();
-    for (int idx = tid; idx < 64 * (N / 8); idx += K::NT) {
-      const int r = idx / (N / 8), c8 = (idx % (N / 8)) * 8;
-      const int64_t t = tok0 + jb * 64 + r;
-      bf16x8 v;
-      if (t < L) {
-        v = *(const bf16x8*)(Bm + (((int64_t)b * L + t) * G + g) * ldn + ncol0 + c8);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = f2bf(0.f);
+    for (int it = 0; it < SIT; ++it) {
+      const int idx = tid + it * K::NT;
+      if (idx < 64 * (N / 8)) {
+        const int r = idx / (N / 8), c8 = (idx % (N / 8)) * 8;
+        *(bf16x8*)(Bs + r * BROW + c8) = sv[it];
       }
-      *(bf16x8*)(Bs + r * BROW + c8) = v;
     }
+    if (jb + 1 < Q / 64) stage_load(jb + 1);
     lds_barrier();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
