@@ -38,25 +38,57 @@ def grouped_path(w):
             and w.chunk_size in (64, 128, 256))
 
 
-def span_plan(w, cus=256):
-    """(span length K, heads per workgroup R) of the forward's span path, or
-    None where the library runs chunk_state + state_passing (same rule as
-    the library's dispatch: spans of 8, else 4, chunks while the grid gives
-    every CU two (batch, span, head) units, else one; R = 4, 2 or 1 heads of a group likewise, at most 2
-    at N = 128 and 1 at N = 64)."""
+def span_scan_chunks(w, cus=256):
+    """The forward's span length at state size 64 (span_scan, an even number
+    of heads per group): the longest span of 8, 4 or 2 chunks whose
+    span_scan grid gives every CU a workgroup; 0 where none does and at every
+    other state size (same rule as the library)."""
+    if not (grouped_path(w) and w.dstate == 64):
+        return 0
+    hg = w.nheads // w.ngroups
+    if hg % 2:
+        return 0
+    for K in (8, 4, 2):
+        if w.nchunks < K:
+            continue
+        ng = -(-w.nchunks // K)
+        R = 4 if (hg % 4 == 0 and w.batch * ng * w.nheads // 4 >= cus) else 2
+        if w.batch * ng * w.nheads // R >= cus:
+            return K
+    return 0
+
+
+def span_plan(w, cus=256, forward=True):
+    """(span length K, heads per workgroup R of span_end and the replay) of
+    the span path, or None where the library runs chunk_state +
+    state_passing (same rule as the library's dispatch: spans of 8, else 4,
+    chunks while the grid gives every CU two (batch, span, head) units, else
+    one; in the forward at state size 64, the span length span_scan's grid
+    asks for; R = 4, 2 or 1 heads of a group likewise, at most 2 at N = 128
+    and 1 at N = 64).  forward=False: the backward's recompute, which keeps
+    the first rule."""
     if not grouped_path(w):
         return None
     nc = w.nchunks
     max_r = 1 if w.dstate == 64 else 2 if w.dstate == 128 else 4
+
+    def heads(K):
+        ng = -(-nc // K)
+        for R in (4, 2):
+            if (R <= max_r and (w.nheads // w.ngroups) % R == 0
+                    and w.batch * ng * w.nheads // R >= cus):
+                return R
+        return 1
+
+    if forward:
+        K = span_scan_chunks(w, cus)
+        if K:
+            return K, heads(K)
     for want in (2 * cus, cus):
         for K in (8, 4):
             ng = -(-nc // K)
             if nc >= K and w.batch * w.nheads * ng >= want:
-                for R in (4, 2):
-                    if (R <= max_r and (w.nheads // w.ngroups) % R == 0
-                            and w.batch * ng * w.nheads // R >= cus):
-                        return K, R
-                return K, 1
+                return K, heads(K)
     return None
 
 
@@ -477,7 +509,7 @@ def stage_sources(stage, direction="forward", workload_name=None):
     (chunk_state, state_passing) run the forward's span kernels where the
     workload takes the span path."""
     if (direction == "backward" and stage in ("chunk_state", "state_passing")
-            and workload_name is not None and span_plan(workload(workload_name))):
+            and workload_name is not None and span_plan(workload(workload_name), forward=False)):
         return KERNEL_SOURCES["span_end"]
     return KERNEL_SOURCES[stage]
 
@@ -703,7 +735,7 @@ def backward_model(w):
     th = B * nc * H * (N // 64) * Q * 4
     fwd = stage_model(w)
     m = {k: fwd[k] for k in ("chunk_cumsum", "chunk_state", "state_passing")}
-    if span_plan(w):
+    if span_plan(w, forward=False):
         # the chunk-start states recomputed over spans, as the forward does:
         # the profile's two stages are span_end and the jump plus the replay
         m["chunk_state"], m["state_passing"] = fwd["span_end"], fwd["span_pass"]

@@ -138,7 +138,11 @@ struct Workspace {
 Workspace plan(const m2::Dims& d) {
   Workspace w;
   w.grouped = m2::grouped_scan_supported(d);
-  w.K = w.grouped ? m2::span_chunks(d) : 0;
+  w.K = 0;
+  if (w.grouped) {
+    w.K = m2::span_scan_chunks(d);
+    if (!w.K) w.K = m2::span_chunks(d);
+  }
   w.Rs = w.K ? m2::span_scan_heads(d, w.K) : 0;
   w.cs_bytes = round256((size_t)(d.B * d.H * d.nc * d.Q) * sizeof(float));
   const size_t hst = round256((size_t)(d.B * d.nc * d.H * d.P * d.N) * 2);

@@ -139,12 +139,6 @@ __device__ __forceinline__ float row_scan16(float v) {
   v = row_shr_add<0x114>(v);
   return row_shr_add<0x118>(v);
 }
-// Value of the previous lane of the row (0 in its first lane).
-__device__ __forceinline__ float row_prev(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false));
-}
-
 typedef short s16x4v __attribute__((ext_vector_type(4)));
 
 // D(16x16, f32) += A(16x16, bf16) * B(16x16, bf16): lane l holds A row (l & 15)

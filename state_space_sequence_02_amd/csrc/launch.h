@@ -109,6 +109,8 @@ hipError_t launch_fwd_pass_state_span(const Dims& d, int K, const void* x, const
 // span_scan_heads gives the heads per workgroup (0 = not covered: the replay
 // and the grouped chunk_scan run instead).
 int span_scan_heads(const Dims& d, int K);
+// The forward's span length where span_scan runs (0 = span_chunks decides).
+int span_scan_chunks(const Dims& d);
 hipError_t launch_span_scan(const Dims& d, int K, int R, const void* x, const void* B,
                             const void* C, const float* dA_cs, const float* dt_T,
                             const float* span_states, const float* D, void* y, hipStream_t s);

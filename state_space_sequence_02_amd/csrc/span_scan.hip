@@ -568,6 +568,30 @@ int span_scan_heads(const Dims& d, int K) {
   return 0;
 }
 
+int span_scan_chunks(const Dims& d) {
+  // At state size 64 span_scan carries most of the step, so its grid
+  // decides: the longest span (8, 4 or 2 chunks) whose span_scan grid
+  // still gives every CU a workgroup (L = 8K, H = 32: spans of 2 instead of
+  // 4, twice the workgroups, 0.103 -> 0.068 ms per step).  0 elsewhere, and
+  // where no span length does (span_end's rule, span_chunks, then decides).
+  // At state size 128 the same rule measured no faster (L = 8K: 0.1106 ->
+  // 0.1113 ms; span_scan's throughput there did not grow with its grid),
+  // nor did spans of one chunk in place of the split path (L = 4K, N = 64:
+  // 0.0433 -> 0.0437 ms).
+  if (!(d.bf16 && d.P == 64 && d.N == 64 && (d.Q == 64 || d.Q == 128 || d.Q == 256)))
+    return 0;
+  const int64_t HG = d.H / d.G;
+  if (HG % 2 != 0) return 0;
+  const int64_t cus = cu_count_scan();
+  for (int K = 8; K >= 2; K /= 2) {
+    if (d.nc < K) continue;
+    const int64_t ng = (d.nc + K - 1) / K;
+    const int64_t R = (HG % 4 == 0 && d.B * ng * d.H / 4 >= cus) ? 4 : 2;
+    if (d.B * ng * d.H / R >= cus) return K;
+  }
+  return 0;
+}
+
 hipError_t launch_span_scan(const Dims& d, int K, int R, const void* x, const void* B,
                             const void* C, const float* dA_cs, const float* dt_T,
                             const float* span_states, const float* D, void* y, hipStream_t s) {

@@ -2,7 +2,9 @@
 
 For bfloat16 with headdim 64, state size 64, 128 or 256 and enough
 (batch, head, span) work to give every CU a workgroup, mamba2_ssd_forward
-runs fwd_pass_state over spans of K = 8 (else 4) chunks: span-end states,
+runs fwd_pass_state over spans of K = 8 (else 4) chunks, or, at state size
+64, the longest of 8, 4 or 2 chunks that fills the device with span_scan
+workgroups: span-end states,
 the jump across spans, and then either a replay of every span that writes the
 chunk-start states for the grouped chunk_scan (state size 256 and 512), or
 span_scan, the replay fused with the output stage (state size 64 and 128),
@@ -37,7 +39,7 @@ def _w(name, L, H, N, G, Q, Bn=1, init=True, seed=0):
 
 
 SHAPES = [
-    _w("span_Q64_N64_G2_K4", 1000, 64, 64, 2, 64, seed=91),
+    _w("span_Q64_N64_G2_K2", 1000, 64, 64, 2, 64, seed=91),
     _w("span_Q64_N256_last_span_one_chunk", 2085, 32, 256, 1, 64, Bn=2, seed=92),
     _w("span_Q128_N128_G3_K4", 5115, 48, 128, 3, 128, init=False, seed=93),
     _w("span_Q256_N64_G4_ragged", 3996, 64, 64, 4, 256, seed=94),
@@ -63,20 +65,33 @@ SHAPES = [
 ]
 
 # (span length, heads per workgroup) each shape reaches on a 256-CU device
-EXPECT = {"span_Q64_N256_last_span_one_chunk": (4, 2), "span_Q64_N256_R4_ragged": (8, 4),
+EXPECT = {"span_Q64_N64_G2_K2": (2, 1), "span_Q64_N256_last_span_one_chunk": (4, 2), "span_Q64_N256_R4_ragged": (8, 4),
           "span_Q128_N128_G2_R2": (8, 2), "span_Q256_N64_G4_R1": (8, 1),
           "span_Q64_N64_R1_ragged": (8, 1), "span_Q64_N512_G4_R4_ragged": (8, 4),
           "span_Q256_N512_G3_K4": (4, 1), "span_Q64_N256_G2_R1_two_per_cu": (8, 1)}
 
 
-def span_chunks(w, cus):
-    """The span length the library picks for these sizes (0: no span path):
-    8 chunks if that gives every CU two (batch, span, head) units, else 4 if
-    that does, else the longest span that gives every CU one."""
+def span_chunks(w, cus, forward=True):
+    """The span length the forward picks for these sizes (0: no span path);
+    forward=False: the backward's recompute, which keeps span_end's rule.
+    At state size 64 with an even number of heads per group (span_scan): the
+    longest span of 8, 4 or 2 chunks whose span_scan grid gives every CU a
+    workgroup.  Otherwise, or if none does: 8 chunks if that gives every CU
+    two (batch, span, head) units, else 4 if that does, else the longest span
+    that gives every CU one."""
     if not (w.dtype == "bf16" and w.headdim == 64 and w.dstate in (64, 128, 256, 512)
             and w.chunk_size in (64, 128, 256)):
         return 0
     nc = -(-w.seqlen // w.chunk_size)
+    hg = w.nheads // w.ngroups
+    if forward and w.dstate == 64 and hg % 2 == 0:
+        for K in (8, 4, 2):
+            if nc < K:
+                continue
+            ng = -(-nc // K)
+            R = 4 if (hg % 4 == 0 and w.batch * ng * w.nheads // 4 >= cus) else 2
+            if w.batch * ng * w.nheads // R >= cus:
+                return K
     for want in (2 * cus, cus):
         for K in (8, 4):
             if nc >= K and w.batch * w.nheads * (-(-nc // K)) >= want:

@@ -23,7 +23,8 @@ def m2():
 
 
 CALLS = [
-    # span path (bf16 start states in the scratch), then the smaller split path
+    # span path (span states in the scratch; span_scan at this state size),
+    # then the smaller split path
     ssd_inputs.custom(name="noalloc_span_L1000_N64", batch=1, seqlen=1000, nheads=64,
                       headdim=64, dstate=64, ngroups=2, chunk_size=64, init_state=True, seed=111),
     ssd_inputs.WORKLOADS["small_L1k_N64"],
