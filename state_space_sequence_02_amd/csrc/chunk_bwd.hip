@@ -663,33 +663,65 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
         rsum[r] = 0.f;
       }
     };
+    // cs of this lane's rows in its two strips (rows past the sequence end
+    // hold a repeated row: masked through vq)
+    const int vq = valid < Q ? (int)valid : Q;
+    float ci[2][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ci[0][r] = css[w * 16 + 4 * grp + r];
+      ci[1][r] = css[(QT - 1 - w) * 16 + 4 * grp + r];
+    }
+    // Software pipeline over the wave's tiles: while tile k's elementwise
+    // work runs, the MFMAs of tile k + 1 (operands read during tile k - 1)
+    // and the LDS reads of tile k + 2 are in flight.
+    bf16x8 oa[2], ob[2];
+    float ocs[2], odt[2];  // column cs and dt of tiles k + 1 (even/odd slot)
+    auto read_tile = [&](int k) {
+      const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        oa[kk] = *(const bf16x8*)(Ys + t64(ti * 16 + L16, 32 * kk + 8 * grp));
+        ob[kk] = *(const bf16x8*)(Xs + t64(tj * 16 + L16, 32 * kk + 8 * grp));
+      }
+      ocs[k & 1] = css[tj * 16 + L16];
+      odt[k & 1] = dts[tj * 16 + L16];
+    };
+    auto tile_mma = [&]() {
+      f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
+      a4 = mfma16x16x32(oa[0], ob[0], a4);
+      return mfma16x16x32(oa[1], ob[1], a4);
+    };
+    read_tile(0);
+    f32x4 an = tile_mma();
+    read_tile(1);
 #pragma unroll
     for (int k = 0; k < SLOTS; ++k) {
       const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
-      f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(Ys + t64(ti * 16 + L16, 32 * kk + 8 * grp));
-        const bf16x8 bb = *(const bf16x8*)(Xs + t64(tj * 16 + L16, 32 * kk + 8 * grp));
-        a4 = mfma16x16x32(a, bb, a4);
-      }
+      const f32x4 a4 = an;
+      const float csj = ocs[k & 1], dtj = odt[k & 1];
+      if (k + 1 < SLOTS) an = tile_mma();
+      if (k + 2 < SLOTS) read_tile(k + 2);
       const int j = tj * 16 + L16;
-      const float csj = css[j], dtj = dts[j];
+      const bool first = k <= w;  // wave-uniform: tile of the strip of row tile w
       float col = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = ti * 16 + 4 * grp + r;
-        // rows past the sequence end hold a repeated row: masked here
-        const float e = (i >= j && i < valid) ? fast_exp2(fminf(css[i] - csj, 0.f)) * dtj : 0.f;
+        const float d = fminf((first ? ci[0][r] : ci[1][r]) - csj, 0.f);
+        const float ev = fast_exp2(d) * dtj;
+        const float e = (i >= j && i < vq) ? ev : 0.f;
         const float wm = e * a4[r];
         ws[k][r] += wm;
         const float t = (i > j) ? cb[k][r] * wm : 0.f;
         rsum[r] += t;
         col += t;
       }
+      // column j's total over the four lane groups, added into its LDS part
+      // by the first group (an add without return: nothing waits for it)
       col += __shfl_xor(col, 16, 64);
       col += __shfl_xor(col, 32, 64);
-      if (grp == 0) part[j] += col;
+      if (grp == 0) __hip_atomic_fetch_add(part + j, col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if (k == w) flush_rows(w);  // end of the first strip (wave-uniform)
       __builtin_amdgcn_sched_barrier(0);
     }
