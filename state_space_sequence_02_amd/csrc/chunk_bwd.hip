@@ -380,22 +380,26 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
       ts += __shfl_xor(ts, 32, 64);
       if (grp == 0) tsv[j] = dts[j] * ts;  // T^S_j
 
+      const float csj = css[j];
 #pragma unroll
       for (int k = 0; k < SLOTS; ++k) {
         if (cslot_strip<QT>(w, k) == s) {
+          // the slot's dY^T operands and row cs, all read before any is used
           const int ti = cslot_ti<QT>(w, k);
-          const float csj = css[j];
+          const int yr = ti * 16 + 4 * grp + (L16 >> 2);
+          bf16x4 ya[4];
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) ya[pt] = lds_read_tr(Ys + t64(yr, pt * 16 + 4 * (L16 & 3)));
+          const f32x4 yc = *(const f32x4*)(css + ti * 16 + 4 * grp);
           bf16x4 bop;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = ti * 16 + 4 * grp + r;
-            const float e = fast_exp2(fminf(css[i] - csj, 0.f));
-            bop[r] = f2bf(i >= j ? cb[k][r] * e : 0.f);
+            const float e = fast_exp2(fminf(yc[r] - csj, 0.f)) * cb[k][r];
+            bop[r] = f2bf(i >= j ? e : 0.f);
           }
-          const int yr = ti * 16 + 4 * grp + (L16 >> 2);
 #pragma unroll
-          for (int pt = 0; pt < 4; ++pt)
-            acc[pt] = mfma16x16x16(lds_read_tr(Ys + t64(yr, pt * 16 + 4 * (L16 & 3))), bop, acc[pt]);
+          for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16x16x16(ya[pt], bop, acc[pt]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
