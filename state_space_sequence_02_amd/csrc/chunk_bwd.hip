@@ -91,6 +91,12 @@ __device__ __forceinline__ int slot_tj(int w, int k) { return k <= w ? k : k - w
 __device__ __forceinline__ int t64(int r, int col) {
   return r * 64 + ((((col >> 3) ^ (r >> 1)) & 7) << 3) + (col & 7);
 }
+// The same for tiles read only by transposed 8-byte reads of 16 rows
+// 8 g + q (g, q < 4) x 4 column pieces: the chunk permutation follows the
+// row group g, so the 64 lanes' pieces fall evenly on the banks.
+__device__ __forceinline__ int t64g(int r, int col) {
+  return r * 64 + ((((col >> 3) ^ (2 * ((r >> 3) & 3))) & 7) << 3) + (col & 7);
+}
 // Element (r, col) of a [64][N] tile (N/8 chunks per row).
 template <int N>
 __device__ __forceinline__ int tN(int r, int col) {
@@ -104,7 +110,7 @@ __device__ __forceinline__ int tN(int r, int col) {
 // src + r * stride (in elements), rows at or past `valid` are zero.  Every
 // load of the thread is issued before its first LDS write, so the tile costs
 // one memory latency rather than one per 16-byte piece.
-template <int ROWS, int NT>
+template <int ROWS, int NT, bool TG = false>
 __device__ __forceinline__ void load_rows64(bf16* dst, const bf16* __restrict__ src,
                                             int64_t stride, int64_t valid) {
   constexpr int IT = (ROWS * 8 + NT - 1) / NT;
@@ -119,7 +125,8 @@ __device__ __forceinline__ void load_rows64(bf16* dst, const bf16* __restrict__ 
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int s = threadIdx.x + it * NT;
-    if (s < ROWS * 8) *(bf16x8*)(dst + t64(s >> 3, (s & 7) * 8)) = v[it];
+    if (s < ROWS * 8)
+      *(bf16x8*)(dst + (TG ? t64g(s >> 3, (s & 7) * 8) : t64(s >> 3, (s & 7) * 8))) = v[it];
   }
 }
 
@@ -769,7 +776,7 @@ struct BcLds {
 };
 
 // Issues the direct-to-LDS loads of one head's h and g column tiles (64 rows
-// x 64 columns, stored with the t64 chunk order) and its cs and dt rows.
+// x 64 columns, stored with the t64g chunk order) and its cs and dt rows.
 template <int Q>
 __device__ __forceinline__ void issue_head_loads(uint32_t buf, const bf16* __restrict__ hsrc,
                                                  const bf16* __restrict__ gsrc, int N,
@@ -780,7 +787,7 @@ __device__ __forceinline__ void issue_head_loads(uint32_t buf, const bf16* __res
   for (int k = wave_id(); k < 18; k += NW) {
     if (k < 16) {
       const int s = (k & 7) * 64 + lane;  // chunk at LDS position s of the tile
-      const int r = s >> 3, ch = (s & 7) ^ ((r >> 1) & 7);
+      const int r = s >> 3, ch = (s & 7) ^ (2 * ((r >> 3) & 3));
       dma16((k < 8 ? hsrc : gsrc) + (int64_t)r * N + ch * 8, buf + (k >> 3) * 8192 + (k & 7) * 1024);
     } else if (lane < Q / 4) {
       dma16((k == 16 ? cs : dt) + lane * 4, buf + 16384 + (k - 16) * Q * 4);
@@ -853,8 +860,8 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
   load_rows(h0);
   {
     const int64_t row0 = ((int64_t)b * L + tok0) * G + g;
-    load_rows64<Q, NT>(Bs, Bm + row0 * N + nt * 64, (int64_t)G * N, valid);
-    load_rows64<Q, NT>(Cs, Cm + row0 * N + nt * 64, (int64_t)G * N, valid);
+    load_rows64<Q, NT, true>(Bs, Bm + row0 * N + nt * 64, (int64_t)G * N, valid);
+    load_rows64<Q, NT, true>(Cs, Cm + row0 * N + nt * 64, (int64_t)G * N, valid);
   }
 
   f32x4 accC[2][4], accB[2][4];
@@ -865,6 +872,18 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
       accC[s][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       accB[s][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  // this lane's C values of the T^h parts (the same for every head)
+  __syncthreads();
+  bf16x4 cth[2][4];
+  {
+    const int L16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cth[s][ct][r] = Cs[t64g(R[s] * 16 + 4 * grp + r, ct * 16 + L16)];
+  }
 
   for (int hh = 0; hh < HG; ++hh) {
     const int h = h0 + hh;
@@ -911,7 +930,7 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const int r0 = 32 * kk + 8 * grp + (L16 >> 2), c0 = ct * 16 + 4 * (L16 & 3);
-          const int oa = t64(r0, c0), ob = t64(r0 + 4, c0);
+          const int oa = t64g(r0, c0), ob = t64g(r0 + 4, c0);
           const bf16x8 hb = cat(lds_read_tr(Hs + oa), lds_read_tr(Hs + ob));
           const bf16x8 gb = cat(lds_read_tr(Gs + oa), lds_read_tr(Gs + ob));
           tc = mfma16x16x32(aY[s][kk], hb, tc);
@@ -922,7 +941,7 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
           const float vc = eC[r] * tc[r];
           accC[s][ct][r] += vc;
           accB[s][ct][r] += eB[r] * tb[r];
-          thr[r] += vc * bf2f(Cs[t64(R[s] * 16 + 4 * grp + r, ct * 16 + L16)]);
+          thr[r] += vc * bf2f(cth[s][ct][r]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -960,7 +979,7 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int br = 32 * kp + 8 * grp + (L16 >> 2), bcol = ct * 16 + 4 * (L16 & 3);
-        const bf16x8 bb = cat(lds_read_tr(Bs + t64(br, bcol)), lds_read_tr(Bs + t64(br + 4, bcol)));
+        const bf16x8 bb = cat(lds_read_tr(Bs + t64g(br, bcol)), lds_read_tr(Bs + t64g(br + 4, bcol)));
         accC[s][ct] = mfma16x16x32(a, bb, accC[s][ct]);
       }
     }
@@ -975,7 +994,7 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int cr = 32 * kp + 8 * grp + (L16 >> 2), ccol = ct * 16 + 4 * (L16 & 3);
-        const bf16x8 cc = cat(lds_read_tr(Cs + t64(cr, ccol)), lds_read_tr(Cs + t64(cr + 4, ccol)));
+        const bf16x8 cc = cat(lds_read_tr(Cs + t64g(cr, ccol)), lds_read_tr(Cs + t64g(cr + 4, ccol)));
         accB[s][ct] = mfma16x16x32(a, cc, accB[s][ct]);
       }
     }
