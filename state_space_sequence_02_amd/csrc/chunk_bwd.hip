@@ -372,7 +372,6 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
           const bf16x8 a = *(const bf16x8*)(Gs + tN<N>(pt * 16 + L16, 32 * ks + 8 * grp));
           acc[pt] = mfma16x16x32(a, Bop[s][ks], acc[pt]);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
       const float sc = fast_exp2(csL - css[j]);
       float ts = 0.f;
@@ -408,7 +407,6 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
 #pragma unroll
           for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16x16x16(ya[pt], bop, acc[pt]);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
 
       float ex = 0.f;
@@ -943,7 +941,6 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
           accB[s][ct][r] += eB[r] * tb[r];
           thr[r] += vc * bf2f(cth[s][ct][r]);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
       // T^h parts of this column tile: 2^cs_i dy_i . (h C_i) over its 64 columns
       float* tho = th + ((((int64_t)b * nc + c) * H + h) * nT + nt) * Q + R[s] * 16 + 4 * grp;
