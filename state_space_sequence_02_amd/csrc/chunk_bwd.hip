@@ -157,6 +157,16 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
                                                    __builtin_bit_cast(s16x4v, b), c, 0, 0, 0);
 }
 
+// v summed over the four 16-lane groups, in every lane: the lanes hold a
+// 4 x 16 matrix (group k, lane j of the group), which is the B operand of a
+// 16x16x4 float32 MFMA; against an A of ones every output row is the
+// matrix's column sums.  One matrix-core instruction instead of two lane
+// permutes through LDS, each waited for.
+__device__ __forceinline__ float group_sum4(float v) {
+  const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, v, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  return d[0];
+}
+
 // Slot k of wave w in chunk_bwd_dx: the column strips of tiles w and
 // QT-1-w, (w..QT-1, w) then (QT-1-w..QT-1, QT-1-w): QT+1 tiles for every wave.
 template <int QT>
@@ -382,8 +392,7 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
           acc[pt][r] *= sc;
           ts += bf2f(xr[s][pt][r]) * acc[pt][r];
         }
-      ts += __shfl_xor(ts, 16, 64);
-      ts += __shfl_xor(ts, 32, 64);
+      ts = group_sum4(ts);
       if (grp == 0) tsv[j] = dts[j] * ts;  // T^S_j
 
       const float csj = css[j];
@@ -428,8 +437,7 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
           *(bf16x4*)(dx + off + p0) = o;
         }
       }
-      ex += __shfl_xor(ex, 16, 64);
-      ex += __shfl_xor(ex, 32, 64);
+      ex = group_sum4(ex);
       if (grp == 0) exs[j] = ex;
     }
     const float Ah = A[h];
@@ -728,8 +736,7 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
       }
       // column j's total over the four lane groups, added into its LDS part
       // by the first group (an add without return: nothing waits for it)
-      col += __shfl_xor(col, 16, 64);
-      col += __shfl_xor(col, 32, 64);
+      col = group_sum4(col);
       if (grp == 0) __hip_atomic_fetch_add(part + j, col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if (k == w) flush_rows(w);  // end of the first strip (wave-uniform)
       __builtin_amdgcn_sched_barrier(0);
