@@ -692,32 +692,42 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
     // Software pipeline over the wave's tiles: while tile k's elementwise
     // work runs, the MFMAs of tile k + 1 (operands read during tile k - 1)
     // and the LDS reads of tile k + 2 are in flight.
-    bf16x8 oa[2], ob[2];
+    // dY operands of the wave's two row strips, read once per head (every
+    // tile of a strip shares them); the x operands per tile
+    bf16x8 ya[2][2], ob[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      ya[0][kk] = *(const bf16x8*)(Ys + t64(w * 16 + L16, 32 * kk + 8 * grp));
+      ya[1][kk] = *(const bf16x8*)(Ys + t64((QT - 1 - w) * 16 + L16, 32 * kk + 8 * grp));
+    }
     float ocs[2], odt[2];  // column cs and dt of tiles k + 1 (even/odd slot)
     auto read_tile = [&](int k) {
-      const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
+      const int tj = slot_tj<QT>(w, k);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        oa[kk] = *(const bf16x8*)(Ys + t64(ti * 16 + L16, 32 * kk + 8 * grp));
-        ob[kk] = *(const bf16x8*)(Xs + t64(tj * 16 + L16, 32 * kk + 8 * grp));
-      }
+      for (int kk = 0; kk < 2; ++kk) ob[kk] = *(const bf16x8*)(Xs + t64(tj * 16 + L16, 32 * kk + 8 * grp));
       ocs[k & 1] = css[tj * 16 + L16];
       odt[k & 1] = dts[tj * 16 + L16];
     };
-    auto tile_mma = [&]() {
+    auto tile_mma = [&](int k) {
       f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
-      a4 = mfma16x16x32(oa[0], ob[0], a4);
-      return mfma16x16x32(oa[1], ob[1], a4);
+      if (k <= w) {  // wave-uniform: the strip of row tile w
+        a4 = mfma16x16x32(ya[0][0], ob[0], a4);
+        a4 = mfma16x16x32(ya[0][1], ob[1], a4);
+      } else {
+        a4 = mfma16x16x32(ya[1][0], ob[0], a4);
+        a4 = mfma16x16x32(ya[1][1], ob[1], a4);
+      }
+      return a4;
     };
     read_tile(0);
-    f32x4 an = tile_mma();
+    f32x4 an = tile_mma(0);
     read_tile(1);
 #pragma unroll
     for (int k = 0; k < SLOTS; ++k) {
       const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
       const f32x4 a4 = an;
       const float csj = ocs[k & 1], dtj = odt[k & 1];
-      if (k + 1 < SLOTS) an = tile_mma();
+      if (k + 1 < SLOTS) an = tile_mma(k + 1);
       if (k + 2 < SLOTS) read_tile(k + 2);
       const int j = tj * 16 + L16;
       const bool first = k <= w;  // wave-uniform: tile of the strip of row tile w
