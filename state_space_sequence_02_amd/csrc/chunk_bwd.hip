@@ -900,12 +900,26 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
         for (int r = 0; r < 4; ++r) cth[s][ct][r] = Cs[t64g(R[s] * 16 + 4 * grp + r, ct * 16 + L16)];
   }
 
+  // The T^h parts of a head leave one head later, before the next head's
+  // loads: a store issued after those loads would hold up the wait for them
+  // (the vector memory counter retires in issue order) by a store's round
+  // trip at the end of every head.
+  f32x4 thv[2];
+  auto store_th = [&](int hs) {
+    if ((lane & 15) == 15) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        *(f32x4*)(th + ((((int64_t)b * nc + c) * H + hs) * nT + nt) * Q + R[s] * 16 + 4 * (lane >> 4)) =
+            thv[s];
+    }
+  };
   for (int hh = 0; hh < HG; ++hh) {
     const int h = h0 + hh;
     // this head's buffer and rows have landed (and every wave is done with
     // the other buffer)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (hh > 0) store_th(h - 1);
     const unsigned char* cur = smem + S::HEAD + (hh & 1) * S::BUF;
     const bf16* Hs = (const bf16*)cur;
     const bf16* Gs = (const bf16*)(cur + 8192);
@@ -959,15 +973,13 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
           thr[r] += vc * bf2f(cth[s][ct][r]);
         }
       }
-      // T^h parts of this column tile: 2^cs_i dy_i . (h C_i) over its 64 columns
-      float* tho = th + ((((int64_t)b * nc + c) * H + h) * nT + nt) * Q + R[s] * 16 + 4 * grp;
+      // T^h parts of this column tile: 2^cs_i dy_i . (h C_i) over its 64
+      // columns (each row's total in the last lane of its 16)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = row_scan16(thr[r]);  // the row's total in its last lane
-        if (L16 == 15) tho[r] = v;
-      }
+      for (int r = 0; r < 4; ++r) thv[s][r] = row_scan16(thr[r]);
     }
   }
+  store_th(h0 + HG - 1);
 
   // the group's summed W (bfloat16 triangle tiles) into LDS, then the
   // products with B and C
