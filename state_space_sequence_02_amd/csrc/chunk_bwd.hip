@@ -326,18 +326,16 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
   // end); loaded one head ahead, so that no wait inside a head's work would
   // also wait for the next head's direct-to-LDS loads
   bf16x4 xr[2][4];
-  auto load_x = [&](int h) {
+  // (strip s's values as soon as that strip of the previous head is done)
+  auto load_x = [&](int h, int s) {
     const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
     const int64_t xrow0 = (((int64_t)b * L + tok0) * H + h) * P;
+    const int j = J[s] * 16 + L16;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int j = J[s] * 16 + L16;
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        xr[s][pt] = __builtin_bit_cast(bf16x4, (short __attribute__((ext_vector_type(4)))){0, 0, 0, 0});
-        if (j < valid)
-          xr[s][pt] = *(const bf16x4*)(x + xrow0 + (int64_t)j * H * P + pt * 16 + 4 * grp);
-      }
+    for (int pt = 0; pt < 4; ++pt) {
+      xr[s][pt] = __builtin_bit_cast(bf16x4, (short __attribute__((ext_vector_type(4)))){0, 0, 0, 0});
+      if (j < valid)
+        xr[s][pt] = *(const bf16x4*)(x + xrow0 + (int64_t)j * H * P + pt * 16 + 4 * grp);
     }
   };
 
@@ -346,7 +344,8 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
   const int rot = c % nh;
   const auto head_at = [&](int k) { return h0 + (k + rot < nh ? k + rot : k + rot - nh); };
   issue(head_at(0), 0);
-  load_x(head_at(0));
+  load_x(head_at(0), 0);
+  load_x(head_at(0), 1);
   for (int hh = 0; hh < nh; ++hh) {
     const int h = head_at(hh);
     __builtin_amdgcn_s_waitcnt(0);  // this head's buffer and x values landed
@@ -439,11 +438,11 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
       }
       ex = group_sum4(ex);
       if (grp == 0) exs[j] = ex;
+      if (hh + 1 < nh) load_x(head_at(hh + 1), s);
     }
     const float Ah = A[h];
     dd = wave_sum(dd);
     if (lane == 0) red[w] = dd;
-    if (hh + 1 < nh) load_x(head_at(hh + 1));
     lds_barrier();  // LDS only: the loads in flight keep flying
 
     // ---- d(A dt)_k, ddt, and the dA and dD parts (one wave)
