@@ -92,10 +92,13 @@ __device__ __forceinline__ int t64(int r, int col) {
   return r * 64 + ((((col >> 3) ^ (r >> 1)) & 7) << 3) + (col & 7);
 }
 // The same for tiles read only by transposed 8-byte reads of 16 rows
-// 8 g + q (g, q < 4) x 4 column pieces: the chunk permutation follows the
-// row group g, so the 64 lanes' pieces fall evenly on the banks.
+// 8 g + q (g, q < 4) x 4 column pieces.  Such a read is served half a wave
+// (g = 0, 1 or g = 2, 3) at a time; the chunk permutation follows bit 0 of
+// g and bit 1 of q, so within each half the 32 lanes' pieces fall on all 64
+// banks once.
+__device__ __forceinline__ int swz_g(int r) { return 2 * (((r >> 3) & 1) | (((r >> 1) & 1) << 1)); }
 __device__ __forceinline__ int t64g(int r, int col) {
-  return r * 64 + ((((col >> 3) ^ (2 * ((r >> 3) & 3))) & 7) << 3) + (col & 7);
+  return r * 64 + ((((col >> 3) ^ swz_g(r)) & 7) << 3) + (col & 7);
 }
 // Element (r, col) of a [64][N] tile (N/8 chunks per row).
 template <int N>
@@ -801,7 +804,7 @@ __device__ __forceinline__ void issue_head_loads(uint32_t buf, const bf16* __res
   for (int k = wave_id(); k < 18; k += NW) {
     if (k < 16) {
       const int s = (k & 7) * 64 + lane;  // chunk at LDS position s of the tile
-      const int r = s >> 3, ch = (s & 7) ^ (2 * ((r >> 3) & 3));
+      const int r = s >> 3, ch = (s & 7) ^ swz_g(r);
       dma16((k < 8 ? hsrc : gsrc) + (int64_t)r * N + ch * 8, buf + (k >> 3) * 8192 + (k & 7) * 1024);
     } else if (lane < Q / 4) {
       dma16((k == 16 ? cs : dt) + lane * 4, buf + 16384 + (k - 16) * Q * 4);
