@@ -750,6 +750,10 @@ def backward_model(w):
         bytes=2 * x + 2 * bc + 2 * hs + 2 * csb + 2 * bc + th + rs)
     m["dx"] = dict(flops=tok * G * (Q + 1) * N + tok * H * (2 * P * N + (Q + 1) * P),
                    bytes=2 * x + 2 * bc + hs + 2 * csb + th + rs + x + tok * H * 2)
+    if N > 256:
+        # the state term B g^T by its own kernel (g and B read, float32 dU
+        # part written), which dx then reads instead of g
+        m["dx"]["bytes"] += bc + 2 * tok * H * P * 4
     m["param_sums"] = dict(flops=4 * B * nc * H, bytes=2 * B * nc * H * 4 + 2 * H * 4)
     return m
 
@@ -757,8 +761,9 @@ def backward_model(w):
 def backward_fast(w):
     """Whether the MFMA backward kernels cover the workload (else the generic
     float32 backward runs)."""
-    return (w.dtype == "bf16" and w.headdim == 64 and w.dstate in (64, 128, 256)
-            and w.chunk_size in (64, 128, 256))
+    return (w.dtype == "bf16" and w.headdim == 64
+            and ((w.dstate in (64, 128, 256) and w.chunk_size in (64, 128, 256))
+                 or (w.dstate == 512 and w.chunk_size == 256)))
 
 
 def generic_backward_flops(w):

@@ -296,11 +296,12 @@ int mamba2_decode_step(const mamba2_dims* dims, const void* x, const void* dt, c
  * may be NULL), dy [B,L,H,P] (dtype of dims) and dfinal [B,H,P,N] float32
  * (NULL = zero).  The forward quantities the gradients need are recomputed
  * inside (nothing from an earlier forward call is read).
- * Supported: every size the forward accepts.  bfloat16 with headdim 64,
- * dstate 64, 128 or 256 and chunk_size 64, 128 or 256 runs MFMA kernels;
- * every other size (float32, other head sizes, dstate 512 and the other
- * multiples of 16) runs a generic path of float32 vector-ALU kernels without
- * MFMA: exact to float32 rounding, and much slower.  Workspace: at least
+ * Supported: every size the forward accepts.  bfloat16 with headdim 64 and
+ * dstate 64, 128 or 256 with chunk_size 64, 128 or 256, or dstate 512 with
+ * chunk_size 256, runs MFMA kernels; every other size (float32, other head
+ * sizes, dstate 512 with shorter chunks and the other multiples of 16) runs
+ * a generic path of float32 vector-ALU kernels without MFMA: exact to
+ * float32 rounding, and much slower.  Workspace: at least
  * mamba2_ssd_backward_workspace_bytes(dims), 256-byte aligned, contents on
  * return unspecified.  Pointer, stream and error rules as for the forward.
  */
@@ -316,7 +317,8 @@ int mamba2_ssd_backward(const mamba2_dims* dims, const void* x, const void* dt, 
  * Same as mamba2_ssd_backward, then waits and writes the device time of each
  * of its eight stages in milliseconds to stage_ms[0..7]: chunk_cumsum,
  * chunk_state, state_passing (the recomputed forward states), adjoint
- * chunk_state, reverse state_passing, dB/dC kernel, dx kernel, dA/dD sums.
+ * chunk_state, reverse state_passing, dB/dC kernel, dx kernel (at dstate 512
+ * with the kernel forming dx's state term before it), dA/dD sums.
  * On the generic path stage 0 holds the whole pass and the others read 0.
  * For measurement only (creates events, blocks).
  */

@@ -455,9 +455,17 @@ int enqueue_backward(const m2::Dims& d, const void* x, const void* dt, const flo
                                       th, s)
           : e;
   mark();
+  // above N = 256 the state term of dU is formed first, into the float32
+  // state slot (no longer read once the reverse pass has run; it holds
+  // P N >= Q P floats per (chunk, head))
+  float* dus = nullptr;
+  if (m2::backward_state_term_separate(d)) {
+    dus = st;
+    e = e == hipSuccess ? m2::launch_chunk_bwd_dus(d, B, gst, dus, s) : e;
+  }
   e = e == hipSuccess ? m2::launch_chunk_bwd_dx(d, x, dy, B, C, dA_cs, dt_T, gst, dots,
                                                 (int)w.wph, th, rsum, A, D, dx, ddt, dA_part,
-                                                dD_part, s)
+                                                dD_part, dus, s)
                       : e;
   mark();
   e = e == hipSuccess ? m2::launch_bwd_param_sums(d, dA_part, dD_part, dA, D ? dD : nullptr, s)
@@ -489,7 +497,7 @@ int check_backward_args(const mamba2_dims* dims, m2::Dims* d, const void* x, con
   if (D) CHECK(need(dD, "dD"));
   CHECK(maybe(dinit, "dinit"));
   const BwdWorkspace w = plan_backward(*d);
-  if (w.fast && w.wph > 64)  // the dx kernel sums the boundary parts with one wavefront
+  if (w.fast && w.wph > 128)  // the dx kernel's LDS holds at most 128 boundary parts
     return fail(MAMBA2_ERR_UNSUPPORTED, "state too large for the backward pass");
   if (!workspace) return fail(MAMBA2_ERR_WORKSPACE, "workspace is NULL");
   if (((uintptr_t)workspace & 255u) != 0)

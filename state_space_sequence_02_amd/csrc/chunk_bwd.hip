@@ -185,11 +185,17 @@ template <int Q, int N>
 struct DxLds {
   using K = BwdCfg<Q>;
   static constexpr int nT = N / 64;
-  // one head's buffer: g [64][N] (tN order), dY [Q][64] (t64 order), cs, dt,
-  // T^h parts [nT][Q], rectangle sums R [Q], boundary dot parts [64]
-  static constexpr int GS = 0, YS = 64 * N * 2, CS = YS + Q * 128, DT = CS + Q * 4;
+  // the state term comes precomputed (chunk_bwd_dus) above N = 256
+  static constexpr bool EXT = N > 256;
+  // one head's buffer: g [64][N] (tN order; none with EXT), dY [Q][64] (t64
+  // order), cs, dt, T^h parts [nT][Q], rectangle sums R [Q], boundary dot
+  // parts [64]
+  static constexpr int GS = 0, YS = EXT ? 0 : 64 * N * 2, CS = YS + Q * 128, DT = CS + Q * 4;
   static constexpr int TH = DT + Q * 4, RS = TH + nT * Q * 4, DOT = RS + Q * 4;
-  static constexpr int BUF = DOT + 64 * 4;
+  // the reverse pass's boundary dot parts: one per wave of a head there
+  // (256-thread blocks over P N / 4 entries), at least 64 slots
+  static constexpr int NDOT = (64 * N / 4 + 255) / 256 * 4;
+  static constexpr int BUF = DOT + (NDOT > 64 ? NDOT : 64) * 4;
   static constexpr int SM = 2 * BUF;                  // x.dU, T^S [Q] each
   static constexpr int RED = SM + 2 * Q * 4;          // per-wave dy.x parts
   static constexpr int BYTES = RED + 64;
@@ -207,7 +213,7 @@ __device__ __forceinline__ void issue_dx_loads(uint32_t buf, const bf16* __restr
                                                const float* __restrict__ dp, int wph) {
   using S = DxLds<Q, N>;
   constexpr int TH4 = S::nT * Q / 4;  // 16-byte pieces of the T^h parts
-  constexpr int NW = BwdCfg<Q>::NW, KG = N / 8, KY = Q / 8, KTH = (TH4 + 63) / 64;
+  constexpr int NW = BwdCfg<Q>::NW, KG = S::EXT ? 0 : N / 8, KY = Q / 8, KTH = (TH4 + 63) / 64;
   constexpr int KTOT = KG + KY + KTH + 4;
   const int lane = lane_id();
   for (int k = wave_id(); k < KTOT; k += NW) {
@@ -235,6 +241,119 @@ __device__ __forceinline__ void issue_dx_loads(uint32_t buf, const bf16* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// chunk_bwd_dus (state size 512)
+// ---------------------------------------------------------------------------
+// The state term of dU before its row decay, dUs[j, p] = sum_n B[j, n] g[p, n]
+// (g: the gradient reaching the chunk's end, bf16 [P, N]), for a state size
+// whose B operands do not fit beside chunk_bwd_dx's other registers; dx
+// then reads it instead of forming it.  One workgroup per (batch, chunk,
+// group, run of heads), 8 waves, Q = 256: wave w owns the chunk's row tiles
+// w and w + 8, whose B rows stay in registers as MFMA operands for every
+// head of the run.  Each head's g arrives by direct-to-LDS loads into a
+// double buffer, each row's 16-byte chunks permuted by the row's low four
+// bits, so the 16 rows of an operand read fall on distinct banks.  Output
+// float32 [B, L, H, P], in the layout of dx's accumulators: lane (L16, grp)
+// of p tile pt holds rows j = 16 t + L16, columns 16 pt + 4 grp .. + 3.
+template <int N>
+struct DusCfg {
+  static constexpr int Q = 256, P = 64, NW = 8, NT = 512, KB = N / 32;
+  static constexpr int RCH = N / 8;      // 16-byte chunks per g row
+  static constexpr int BUF = P * N * 2;  // one head's g
+  static constexpr int LDS = 2 * BUF;
+  static_assert(RCH % 16 == 0, "row permutation stays inside the row");
+};
+
+__device__ __forceinline__ int gswz(int r, int ch) { return ch ^ (r & 15); }
+
+template <int N>
+__global__ void __launch_bounds__(512, 1) chunk_bwd_dus_kernel(
+    const bf16* __restrict__ Bm, const bf16* __restrict__ gst, float* __restrict__ dus, int L,
+    int H, int G, int nc, int hpw, int slices) {
+  using K = DusCfg<N>;
+  constexpr int P = K::P, Q = K::Q, KB = K::KB;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+  int bid = blockIdx.x;
+  const int slice = bid % slices;
+  bid /= slices;
+  const int g = bid % G;
+  bid /= G;
+  const int c = bid % nc;
+  const int b = bid / nc;
+  const int HG = H / G;
+  const int h0 = g * HG + slice * hpw;
+  const int nh = min(hpw, HG - slice * hpw);
+  if (nh <= 0) return;  // whole workgroup
+
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int L16 = lane & 15, grp = lane >> 4;
+  const int64_t tok0 = (int64_t)c * Q;
+  const int64_t valid = (int64_t)L - tok0;
+  const uint32_t base = lds_addr(smem);
+
+  // head h's g into buffer `buf`: P * N / 512 wave-loads of 1 KB
+  auto issue = [&](int h, int buf) {
+    const bf16* src = gst + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+    for (int k = w; k < P * N / 512; k += K::NW) {
+      const int s = k * 64 + lane;
+      const int r = s / K::RCH, pos = s % K::RCH;
+      dma16(src + (int64_t)r * N + gswz(r, pos) * 8, base + buf * K::BUF + k * 1024);
+    }
+  };
+  const int rot = c % nh;
+  const auto head_at = [&](int k) { return h0 + (k + rot < nh ? k + rot : k + rot - nh); };
+  issue(head_at(0), 0);
+
+  // B operands of this wave's two row tiles (zero past the sequence end)
+  bf16x8 bop[2][KB];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int i = (w + 8 * s) * 16 + L16;
+    const bf16* src = Bm + (((int64_t)b * L + tok0 + i) * G + g) * N + 8 * grp;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      bop[s][kb] = zero8();
+      if (i < valid) bop[s][kb] = *(const bf16x8*)(src + 32 * kb);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int k = 0; k < nh; ++k) {
+    const int h = head_at(k);
+    if (k + 1 < nh) issue(head_at(k + 1), (k + 1) & 1);
+    const bf16* gs = (const bf16*)(smem + (k & 1) * K::BUF);
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) acc[0][pt] = acc[1][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      const int r = pt * 16 + L16;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = *(const bf16x8*)(gs + r * N + gswz(r, 4 * kb + grp) * 8);
+        acc[0][pt] = mfma16x16x32(a, bop[0][kb], acc[0][pt]);
+        acc[1][pt] = mfma16x16x32(a, bop[1][kb], acc[1][pt]);
+      }
+    }
+    // the next head's g has landed (and this wave's older stores drained):
+    // then this head's stores, which the next such wait covers a head later
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int i = (w + 8 * s) * 16 + L16;
+      if (i < valid) {
+        float* dst = dus + (((int64_t)b * L + tok0 + i) * H + h) * P + 4 * grp;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) *(f32x4*)(dst + 16 * pt) = acc[s][pt];
+      }
+    }
+    lds_barrier();  // every wave's g landed; the buffer just read is free
+  }
+}
+
 // The log-decay gradient is formed without cancellation: for position k,
 //   d(A dt)_k = R_k + sum_{i >= k} T^h_i + sum_{j < k} T^S_j + 2^cs_last <g, h_start>,
 // R_k = sum_{i >= k > j} (M o CB)_ij dt_j (dy_i . x_j) (from the summed-W
@@ -248,10 +367,16 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
     const bf16* __restrict__ gst, const float* __restrict__ dots, const float* __restrict__ th,
     const float* __restrict__ rsum, const float* __restrict__ A, const float* __restrict__ D,
     bf16* __restrict__ dx, bf16* __restrict__ ddt, float* __restrict__ dA_part,
-    float* __restrict__ dD_part, int L, int H, int G, int nc, int hpw, int slices, int wph) {
+    float* __restrict__ dD_part, const float* __restrict__ dus, int L, int H, int G, int nc,
+    int hpw, int slices, int wph) {
   using K = BwdCfg<Q>;
   using S = DxLds<Q, N>;
-  constexpr int P = 64, QT = K::QT, NW = K::NW, NT = K::NT, SLOTS = K::SLOTS, KN = N / 32;
+  // EXT: the state term B g^T arrives from chunk_bwd_dus (float32 [B, L, H,
+  // P], before its row decay) instead of being formed here from resident B
+  // operands, which would not fit in the registers at this state size
+  constexpr bool EXT = S::EXT;
+  constexpr int P = 64, QT = K::QT, NW = K::NW, NT = K::NT, SLOTS = K::SLOTS;
+  constexpr int KN = EXT ? 1 : N / 32;
   constexpr int nT = S::nT;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
@@ -302,11 +427,13 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (!EXT) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          Bop[s][2 * ns + kk] = *(const bf16x8*)(Bs + t64(J[s] * 16 + L16, 32 * kk + 8 * grp));
+          for (int kk = 0; kk < 2; ++kk)
+            Bop[s][2 * ns + kk] = *(const bf16x8*)(Bs + t64(J[s] * 16 + L16, 32 * kk + 8 * grp));
+      }
     }
     __syncthreads();  // slices consumed before the head buffers take their space
   }
@@ -329,6 +456,7 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
   // end); loaded one head ahead, so that no wait inside a head's work would
   // also wait for the next head's direct-to-LDS loads
   bf16x4 xr[2][4];
+  f32x4 dsr[2][EXT ? 4 : 1];  // EXT: the precomputed state term, same layout
   // (strip s's values as soon as that strip of the previous head is done)
   auto load_x = [&](int h, int s) {
     const int L16 = opaque(lane & 15), grp = opaque(lane >> 4);
@@ -339,6 +467,10 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
       xr[s][pt] = __builtin_bit_cast(bf16x4, (short __attribute__((ext_vector_type(4)))){0, 0, 0, 0});
       if (j < valid)
         xr[s][pt] = *(const bf16x4*)(x + xrow0 + (int64_t)j * H * P + pt * 16 + 4 * grp);
+      if constexpr (EXT) {
+        dsr[s][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (j < valid) dsr[s][pt] = *(const f32x4*)(dus + xrow0 + (int64_t)j * H * P + pt * 16 + 4 * grp);
+      }
     }
   };
 
@@ -375,14 +507,19 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
     for (int s = 0; s < 2; ++s) {
       const int j = J[s] * 16 + L16;
       f32x4 acc[4];
+      if constexpr (EXT) {
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = dsr[s][pt];
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < KN; ++ks) {
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          const bf16x8 a = *(const bf16x8*)(Gs + tN<N>(pt * 16 + L16, 32 * ks + 8 * grp));
-          acc[pt] = mfma16x16x32(a, Bop[s][ks], acc[pt]);
+        for (int ks = 0; ks < KN; ++ks) {
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) {
+            const bf16x8 a = *(const bf16x8*)(Gs + tN<N>(pt * 16 + L16, 32 * ks + 8 * grp));
+            acc[pt] = mfma16x16x32(a, Bop[s][ks], acc[pt]);
+          }
         }
       }
       const float sc = fast_exp2(csL - css[j]);
@@ -454,7 +591,9 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
       const float* rsv = (const float*)(cur + S::RS);
       const float* thv = (const float*)(cur + S::TH);
       const float* dpv = (const float*)(cur + S::DOT);
-      const float dc = wave_sum(lane < wph ? dpv[lane] : 0.f);
+      float dp = 0.f;
+      for (int i = lane; i < wph; i += 64) dp += dpv[i];
+      const float dc = wave_sum(dp);
       float rk[E], ps[E], sh[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -1080,7 +1219,9 @@ template <int Q, int N>
 hipError_t launch_dx(const Dims& d, const void* x, const void* dy, const void* B, const void* C,
                      const float* dA_cs, const float* dt_T, const void* gst, const float* dots,
                      int wph, const float* th, const float* rsum, const float* A, const float* D,
-                     void* dx, void* ddt, float* dA_part, float* dD_part, hipStream_t s) {
+                     void* dx, void* ddt, float* dA_part, float* dD_part, const float* dus,
+                     hipStream_t s) {
+  if (DxLds<Q, N>::EXT && dus == nullptr) return hipErrorInvalidValue;
   auto kern = chunk_bwd_dx_kernel<Q, N>;
   constexpr int lds = DxLds<Q, N>::BYTES;
   static const hipError_t attr =
@@ -1095,8 +1236,28 @@ hipError_t launch_dx(const Dims& d, const void* x, const void* dy, const void* B
   const int64_t grid = d.B * d.nc * d.G * slices;
   kern<<<(unsigned)grid, BwdCfg<Q>::NT, lds, s>>>(
       (const bf16*)x, (const bf16*)dy, (const bf16*)B, (const bf16*)C, dA_cs, dt_T,
-      (const bf16*)gst, dots, th, rsum, A, D, (bf16*)dx, (bf16*)ddt, dA_part, dD_part, (int)d.L,
-      (int)d.H, (int)d.G, (int)d.nc, (int)hpw, (int)slices, wph);
+      (const bf16*)gst, dots, th, rsum, A, D, (bf16*)dx, (bf16*)ddt, dA_part, dD_part, dus,
+      (int)d.L, (int)d.H, (int)d.G, (int)d.nc, (int)hpw, (int)slices, wph);
+  return hipGetLastError();
+}
+
+template <int N>
+hipError_t launch_dus(const Dims& d, const void* B, const void* gst, float* dus, hipStream_t s) {
+  using K = DusCfg<N>;
+  auto kern = chunk_bwd_dus_kernel<N>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS);
+  if (attr != hipSuccess) return attr;
+  const int64_t HG = d.H / d.G;
+  int64_t hpw = (d.B * d.nc * d.H) / cu_count_bwd();
+  if (hpw < 1) hpw = 1;
+  if (hpw > HG) hpw = HG;
+  const int64_t slices = (HG + hpw - 1) / hpw;
+  hpw = (HG + slices - 1) / slices;
+  const int64_t grid = d.B * d.nc * d.G * slices;
+  kern<<<(unsigned)grid, K::NT, K::LDS, s>>>((const bf16*)B, (const bf16*)gst, dus, (int)d.L,
+                                             (int)d.H, (int)d.G, (int)d.nc, (int)hpw,
+                                             (int)slices);
   return hipGetLastError();
 }
 
@@ -1132,22 +1293,32 @@ hipError_t launch_dbdc(const Dims& d, const void* x, const void* dy, const void*
 }  // namespace
 
 bool backward_supported(const Dims& d) {
-  return d.bf16 && d.P == 64 && (d.N == 64 || d.N == 128 || d.N == 256) &&
-         (d.Q == 64 || d.Q == 128 || d.Q == 256);
+  return d.bf16 && d.P == 64 &&
+         (((d.N == 64 || d.N == 128 || d.N == 256) && (d.Q == 64 || d.Q == 128 || d.Q == 256)) ||
+          (d.N == 512 && d.Q == 256));
+}
+
+bool backward_state_term_separate(const Dims& d) { return d.N > 256; }
+
+hipError_t launch_chunk_bwd_dus(const Dims& d, const void* B, const void* gst, float* dus,
+                                hipStream_t s) {
+  if (d.N == 512 && d.Q == 256 && d.P == 64 && d.bf16) return launch_dus<512>(d, B, gst, dus, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_bwd_dx(const Dims& d, const void* x, const void* dy, const void* B,
                                const void* C, const float* dA_cs, const float* dt_T,
                                const void* gst, const float* dots, int wph, const float* th,
                                const float* rsum, const float* A, const float* D, void* dx,
-                               void* ddt, float* dA_part, float* dD_part, hipStream_t s) {
+                               void* ddt, float* dA_part, float* dD_part, const float* dus,
+                               hipStream_t s) {
 #define M2_DX(QQ, NN)                                                                         \
   if (d.Q == QQ && d.N == NN)                                                                 \
     return launch_dx<QQ, NN>(d, x, dy, B, C, dA_cs, dt_T, gst, dots, wph, th, rsum, A, D, dx, \
-                             ddt, dA_part, dD_part, s);
+                             ddt, dA_part, dD_part, dus, s);
   M2_DX(64, 64) M2_DX(64, 128) M2_DX(64, 256)
   M2_DX(128, 64) M2_DX(128, 128) M2_DX(128, 256)
-  M2_DX(256, 64) M2_DX(256, 128) M2_DX(256, 256)
+  M2_DX(256, 64) M2_DX(256, 128) M2_DX(256, 256) M2_DX(256, 512)
 #undef M2_DX
   return hipErrorInvalidValue;
 }

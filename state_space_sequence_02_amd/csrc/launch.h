@@ -64,7 +64,14 @@ hipError_t launch_chunk_bwd_dx(const Dims& d, const void* x, const void* dy, con
                                const void* C, const float* dA_cs, const float* dt_T,
                                const void* gst, const float* dots, int wph, const float* th,
                                const float* rsum, const float* A, const float* D, void* dx,
-                               void* ddt, float* dA_part, float* dD_part, hipStream_t s);
+                               void* ddt, float* dA_part, float* dD_part, const float* dus,
+                               hipStream_t s);
+// Above N = 256 (backward_state_term_separate): the state term of dU before
+// its row decay, dus[B,L,H,P] f32 = B g^T per (chunk, head), which
+// launch_chunk_bwd_dx then reads (dus non-NULL) instead of forming it.
+bool backward_state_term_separate(const Dims& d);
+hipError_t launch_chunk_bwd_dus(const Dims& d, const void* B, const void* gst, float* dus,
+                                hipStream_t s);
 hipError_t launch_bwd_param_sums(const Dims& d, const float* dA_part, const float* dD_part,
                                  float* dA, float* dD, hipStream_t s);
 

@@ -169,11 +169,12 @@ def test_backward_checks_on_host():
         args.update(over)
         return lib.mamba2_ssd_backward(ctypes.byref(dims), *args.values(), 0)
 
-    # float32, headdim 32 and state size 512 take the generic backward: its
+    # float32, headdim 32 and state size 512 at chunk 64 take the generic
+    # backward, state size 512 at chunk 256 the MFMA kernels: either way the
     # workspace holds at least the cumulative sums, dt and two float32 state
-    # arrays, and its argument checks are those of the MFMA path
+    # arrays' worth, and the argument checks are the same
     for kw in (dict(dtype=m2.MAMBA2_DTYPE_F32, headdim=16, dstate=16, nheads=2, chunk_size=64),
-               dict(headdim=32), dict(dstate=512)):
+               dict(headdim=32), dict(dstate=512, chunk_size=64), dict(dstate=512)):
         dd = _dims(**kw)
         assert m2.mamba2_validate(dd) == m2.MAMBA2_OK
         nc = -(-dd.seqlen // dd.chunk_size)

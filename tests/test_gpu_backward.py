@@ -44,6 +44,11 @@ SHAPES = [
     _w("bwd_Q64_N128_G1_H8", 333, 8, 128, 1, 64, seed=68),
     _w("bwd_one_token", 1, 4, 128, 2, 128, Bn=2, seed=72),
     _w("bwd_Q128_N256_heads_eq_groups", 257, 3, 256, 3, 128, Bn=3, seed=73),
+    # state size 512 (chunk 256): the state term of dU formed by its own
+    # kernel, ragged last chunk, two batches, heads in two and four groups
+    _w("bwd_Q256_N512_G2", 600, 4, 512, 2, 256, seed=85),
+    _w("bwd_Q256_N512_G4_B2_ragged", 777, 8, 512, 4, 256, Bn=2, seed=92),
+    _w("bwd_Q256_N512_short", 100, 2, 512, 1, 256, init=False, seed=93),
 ]
 
 NAMES = ("dx", "ddt", "dA", "dB", "dC", "dD", "dinit")
@@ -136,8 +141,8 @@ def test_backward_recompute_over_spans(m2):
     say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
-def test_backward_writes_only_its_outputs(m2):
-    w = SHAPES[4]
+@pytest.mark.parametrize("w", [SHAPES[4], SHAPES[-2]], ids=lambda w: w.name)
+def test_backward_writes_only_its_outputs(m2, w):
     inp = ssd_inputs.make_inputs(w)
     cot = ssd_inputs.make_cotangents(w)
     g = to_gpu(inp)
@@ -168,7 +173,8 @@ def _wg(name, L, H, P, N, G, Q, Bn=1, init=True, seed=0, dtype="bf16"):
 
 # Sizes the MFMA backward does not cover run the generic backward (float32
 # arithmetic on the vector ALU): float32 inputs, head sizes other than 64,
-# state sizes other than 64/128/256 (512 included).  The shapes put 1 to 4
+# state sizes other than 64/128/256/512 and state size 512 with chunks
+# shorter than 256.  The shapes put 1 to 4
 # output tiles of 64 along the chunk, the head size and the state size, with
 # ragged tiles, ragged last chunks, a sequence shorter than one chunk and a
 # single token.
@@ -177,7 +183,7 @@ GENERIC = [
     _wg("gbwd_f32_Q16_P32_N16", 70, 2, 32, 16, 1, 16, dtype="f32", seed=82),
     _wg("gbwd_f32_Q256_P80_N100", 300, 2, 80, 100, 1, 256, dtype="f32", init=False, seed=83),
     _wg("gbwd_bf16_P32_N64", 300, 4, 32, 64, 2, 128, seed=84),
-    _wg("gbwd_bf16_P64_N512_G2", 600, 4, 64, 512, 2, 256, seed=85),
+    _wg("gbwd_bf16_P64_N512_G2_Q128", 600, 4, 64, 512, 2, 128, seed=85),
     _wg("gbwd_bf16_P64_N512_Q64", 333, 4, 64, 512, 4, 64, Bn=2, seed=86),
     _wg("gbwd_bf16_P128_N96", 257, 2, 128, 96, 1, 128, seed=87),
     _wg("gbwd_bf16_P48_N208_short", 40, 3, 48, 208, 3, 64, seed=88),
@@ -195,7 +201,7 @@ def test_generic_backward_matches_oracle(m2, w):
 
 
 def test_generic_backward_without_D_or_final_gradient(m2):
-    for w in (GENERIC[0], GENERIC[4]):
+    for w in (GENERIC[0], GENERIC[4]):  # float32; bf16 at N = 512, chunk 128
         got, ref = _run(m2, w, with_D=False, with_dfinal=False)
         assert got["dD"] is None
         _compare(got, ref, GTOL[w.dtype])
@@ -233,22 +239,55 @@ def test_generic_backward_writes_only_its_outputs(m2, w):
 
 
 def test_generic_backward_multichunk_N512(m2):
-    """16 chunks of 256 at the largest state (N = 512), 8 heads in 2 groups:
+    """16 chunks of 128 at the largest state (N = 512), 8 heads in 2 groups:
     the generic backward across many chunk boundaries."""
-    w = _wg("gbwd_long_L4096_N512", 4096, 8, 64, 512, 2, 256, seed=90)
+    w = _wg("gbwd_long_L2048_N512_Q128", 2048, 8, 64, 512, 2, 128, seed=90)
     say(f"backward (generic) {w.name}")
     got, ref = _run(m2, w)
     errs = _compare(got, ref)
     say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
-def test_generic_backward_fullsize_properties(m2):
+def test_backward_multichunk_N512(m2):
+    """16 chunks of 256 at the largest state (N = 512), 8 heads in 2 groups:
+    the MFMA backward with the separate state-term kernel across many chunk
+    boundaries (over spans of chunks in the recompute)."""
+    w = _wg("bwd_long_L4096_N512", 4096, 8, 64, 512, 2, 256, seed=90)
+    say(f"backward {w.name}")
+    got, ref = _run(m2, w)
+    errs = _compare(got, ref)
+    say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+def test_backward_N512_takes_the_mfma_path(m2):
+    """At N = 512 with chunk 256 every stage of the profile entry runs (the
+    generic path reports its whole time as stage 0 and 0 for the others)."""
+    w = SHAPES[-3]
+    inp = ssd_inputs.make_inputs(w)
+    cot = ssd_inputs.make_cotangents(w)
+    g = to_gpu(inp)
+    dims = m2.dims_of(g["x"], g["B"], w.chunk_size)
+    need = m2.mamba2_ssd_backward_workspace_bytes(dims)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = {k: torch.empty_like(g[s]) for k, s in (("dx", "x"), ("ddt", "dt"), ("dB", "B"),
+                                                  ("dC", "C"))}
+    dA = torch.empty(w.nheads, dtype=torch.float32, device="cuda")
+    dD = torch.empty_like(dA)
+    dinit = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device="cuda")
+    ms = m2.mamba2_ssd_backward_profile(dims, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"],
+                                        g["init_state"], cot["dy"].cuda(), cot["dfinal"].cuda(),
+                                        out["dx"], out["ddt"], dA, out["dB"], out["dC"], dD, dinit,
+                                        ws, need)
+    assert len(ms) == 8 and all(v > 0 for v in ms[1:7]), ms
+
+
+def test_backward_fullsize_properties_N512(m2):
     """L = 262144, H = 32, P = 64, N = 512, G = 4, Q = 256 (the largest-state
-    workload) through the generic backward: finite gradients, dD equal to
+    workload) through the MFMA backward: finite gradients, dD equal to
     sum(dy * x), and gradients homogeneous in the upstream gradient."""
-    w = ssd_inputs.custom(name="gbwd_full", batch=1, seqlen=262144, nheads=32, headdim=64,
+    w = ssd_inputs.custom(name="bwd_full_N512", batch=1, seqlen=262144, nheads=32, headdim=64,
                           dstate=512, ngroups=4, chunk_size=256, init_state=False, seed=91)
-    say(f"backward (generic) {w.name}")
+    say(f"backward {w.name}")
     inp = ssd_inputs.make_inputs(w)
     cot = ssd_inputs.make_cotangents(w)
     g = to_gpu(inp)
