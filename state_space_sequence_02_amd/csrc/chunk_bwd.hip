@@ -25,23 +25,25 @@
 // equal totals and loses the result to rounding).  <g, h> comes from the
 // reverse state pass, T^h from chunk_bwd_dbdc.
 //
-// Two kernels share the work.  chunk_bwd_dx: one workgroup per (batch, chunk,
-// group, run of heads); C B^T of the group is formed once and kept in float32
-// accumulators; per head the masked, decayed tiles go to LDS as bfloat16 and
-// feed dU^T = dY^T (M o CB) + ...; the epilogue forms dx, the row dot
-// products, the rectangle sums of T, ddt and the per-chunk parts of dA, dD.
-// chunk_bwd_wsum: one workgroup per (batch, chunk, group); per head W is
-// formed, masked and accumulated over the group's heads in float32 registers
-// (the group sum is taken before the products with B and C, so those run
-// once per group rather than once per head).  chunk_bwd_dbdc: one workgroup
-// per (batch, chunk, group, 64 state columns); per head the state terms (and
-// their T^h parts) accumulate in registers; the products of the summed W with
-// B and C follow once, from LDS.
+// Four kernels share the work.  chunk_bwd_wsum: one workgroup per (batch,
+// chunk, group); per head W is formed, masked and accumulated over the
+// group's heads in float32 registers (the group sum is taken before the
+// products with B and C, so those run once per group rather than once per
+// head), with the rectangle sums of T.  chunk_bwd_dbdc: one workgroup per
+// (batch, chunk, group, 64 state columns); per head the state terms (and
+// their T^h parts) accumulate in registers; the products of the summed W
+// with B and C follow once, from LDS.  chunk_bwd_dx: one workgroup per
+// (batch, chunk, group, run of heads); C B^T of the group is formed once
+// and kept in float32 accumulators; per head the masked, decayed tiles feed
+// dU^T = dY^T (M o CB) + ... as MFMA operands straight from registers; the
+// epilogue forms dx, the row dot products, ddt and the per-chunk parts of
+// dA, dD.  Above state size 256, chunk_bwd_dus first forms dx's state term
+// B g^T, which dx then reads.
 //
-// Both use 16x16x32 bfloat16 MFMA.  chunk_bwd_dx runs Q/32 waves; wave w owns
-// the output column tiles w and Q/16-1-w (equal causal work per wave) and the
-// lower-triangle tiles of the Q x Q interaction matrix in the row strips of
-// those two tiles (Q/16 + 1).
+// All use bfloat16 MFMA with float32 accumulation.  chunk_bwd_dx runs Q/32
+// waves; wave w owns the output column tiles w and Q/16-1-w (equal causal
+// work per wave) and the lower-triangle tiles of the Q x Q interaction
+// matrix in the column strips of those two tiles (Q/16 + 1).
 #include "common.h"
 #include "launch.h"
 
