@@ -111,28 +111,43 @@ __device__ __forceinline__ int tN(int r, int col) {
     return t64(r, col);
 }
 
-// rows [ROWS][64] of bfloat16 into an LDS tile; row r comes from
-// src + r * stride (in elements), rows at or past `valid` are zero.  Every
-// load of the thread is issued before its first LDS write, so the tile costs
-// one memory latency rather than one per 16-byte piece.
+// rows [ROWS][64] of bfloat16 in registers on their way into an LDS tile;
+// row r comes from src + r * stride (in elements), rows at or past `valid`
+// are zero.  load() issues every 16-byte load of the thread before store()
+// writes the first one, so a tile costs one memory latency rather than one
+// per piece, and a caller can keep the next tile's loads in flight while it
+// works on the current one.
+template <int ROWS, int NT>
+struct RowSlab {
+  static constexpr int IT = (ROWS * 8 + NT - 1) / NT;
+  bf16x8 v[IT];
+  __device__ __forceinline__ void load(const bf16* __restrict__ src, int64_t stride,
+                                       int64_t valid) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int s = threadIdx.x + it * NT;
+      const int r = s >> 3, ch = s & 7;
+      v[it] = zero8();
+      if (s < ROWS * 8 && r < valid) v[it] = *(const bf16x8*)(src + (int64_t)r * stride + ch * 8);
+    }
+  }
+  template <bool TG = false>
+  __device__ __forceinline__ void store(bf16* dst) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int s = threadIdx.x + it * NT;
+      if (s < ROWS * 8)
+        *(bf16x8*)(dst + (TG ? t64g(s >> 3, (s & 7) * 8) : t64(s >> 3, (s & 7) * 8))) = v[it];
+    }
+  }
+};
+
 template <int ROWS, int NT, bool TG = false>
 __device__ __forceinline__ void load_rows64(bf16* dst, const bf16* __restrict__ src,
                                             int64_t stride, int64_t valid) {
-  constexpr int IT = (ROWS * 8 + NT - 1) / NT;
-  bf16x8 v[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int s = threadIdx.x + it * NT;
-    const int r = s >> 3, ch = s & 7;
-    v[it] = zero8();
-    if (s < ROWS * 8 && r < valid) v[it] = *(const bf16x8*)(src + (int64_t)r * stride + ch * 8);
-  }
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int s = threadIdx.x + it * NT;
-    if (s < ROWS * 8)
-      *(bf16x8*)(dst + (TG ? t64g(s >> 3, (s & 7) * 8) : t64(s >> 3, (s & 7) * 8))) = v[it];
-  }
+  RowSlab<ROWS, NT> slab;
+  slab.load(src, stride, valid);
+  slab.template store<TG>(dst);
 }
 
 // ---------------------------------------------------------------------------
@@ -412,12 +427,31 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_dx_kernel(
     bf16* Cs = (bf16*)smem;
     bf16* Bs = Cs + Q * 64;
     const int64_t row0 = ((int64_t)b * L + tok0) * G + g;
+    // 64-column slices of C and B.  Above N = 256 (eight slices) the next
+    // slice's loads fly while the current one's MFMAs run (at N = 256 that
+    // measured 5 us slower, so there each slice is loaded, then used).
+    RowSlab<Q, NT> sc, sb;
+    if constexpr (EXT) {
+      sc.load(Cm + row0 * N, (int64_t)G * N, valid);
+      sb.load(Bm + row0 * N, (int64_t)G * N, valid);
+    }
 #pragma unroll
     for (int ns = 0; ns < N / 64; ++ns) {
-      __syncthreads();
-      load_rows64<Q, NT>(Cs, Cm + row0 * N + ns * 64, (int64_t)G * N, valid);
-      load_rows64<Q, NT>(Bs, Bm + row0 * N + ns * 64, (int64_t)G * N, valid);
-      __syncthreads();
+      if constexpr (EXT) {
+        lds_barrier();  // every wave is done with the previous slice
+        sc.store(Cs);
+        sb.store(Bs);
+        if (ns + 1 < N / 64) {
+          sc.load(Cm + row0 * N + (ns + 1) * 64, (int64_t)G * N, valid);
+          sb.load(Bm + row0 * N + (ns + 1) * 64, (int64_t)G * N, valid);
+        }
+        lds_barrier();  // this slice visible to every wave
+      } else {
+        __syncthreads();
+        load_rows64<Q, NT>(Cs, Cm + row0 * N + ns * 64, (int64_t)G * N, valid);
+        load_rows64<Q, NT>(Bs, Bm + row0 * N + ns * 64, (int64_t)G * N, valid);
+        __syncthreads();
+      }
 #pragma unroll
       for (int k = 0; k < SLOTS; ++k) {
         const int ti = cslot_ti<QT>(w, k), tj = cslot_tj<QT>(w, k);
@@ -736,11 +770,20 @@ __global__ void __launch_bounds__(BwdCfg<Q>::NT, 1) chunk_bwd_wsum_kernel(
     bf16* Cs = (bf16*)smem;
     bf16* Bs = Cs + Q * 64;
     const int64_t row0 = ((int64_t)b * L + tok0) * G + g;
+    // 64-column slices of C and B, the next slice's loads in flight while
+    // the current one's MFMAs run
+    RowSlab<Q, NT> sc, sb;
+    sc.load(Cm + row0 * N, (int64_t)G * N, valid);
+    sb.load(Bm + row0 * N, (int64_t)G * N, valid);
     for (int ns = 0; ns < N / 64; ++ns) {
-      __syncthreads();
-      load_rows64<Q, NT>(Cs, Cm + row0 * N + ns * 64, (int64_t)G * N, valid);
-      load_rows64<Q, NT>(Bs, Bm + row0 * N + ns * 64, (int64_t)G * N, valid);
-      __syncthreads();
+      lds_barrier();  // every wave is done with the previous slice
+      sc.store(Cs);
+      sb.store(Bs);
+      if (ns + 1 < N / 64) {
+        sc.load(Cm + row0 * N + (ns + 1) * 64, (int64_t)G * N, valid);
+        sb.load(Bm + row0 * N + (ns + 1) * 64, (int64_t)G * N, valid);
+      }
+      lds_barrier();  // this slice visible to every wave
 #pragma unroll
       for (int k = 0; k < SLOTS; ++k) {
         const int ti = slot_ti<QT>(w, k), tj = slot_tj<QT>(w, k);
