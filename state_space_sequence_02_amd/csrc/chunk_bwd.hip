@@ -1061,8 +1061,11 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
   load_rows(h0);
   {
     const int64_t row0 = ((int64_t)b * L + tok0) * G + g;
-    load_rows64<Q, NT, true>(Bs, Bm + row0 * N + nt * 64, (int64_t)G * N, valid);
-    load_rows64<Q, NT, true>(Cs, Cm + row0 * N + nt * 64, (int64_t)G * N, valid);
+    RowSlab<Q, NT> sb, sc;  // both tiles' loads in flight together
+    sb.load(Bm + row0 * N + nt * 64, (int64_t)G * N, valid);
+    sc.load(Cm + row0 * N + nt * 64, (int64_t)G * N, valid);
+    sb.template store<true>(Bs);
+    sc.template store<true>(Cs);
   }
 
   f32x4 accC[2][4], accB[2][4];
@@ -1173,9 +1176,21 @@ __global__ void __launch_bounds__(BcCfg<Q>::NT, 1) chunk_bwd_dbdc_kernel(
   const int L16 = lane & 15, grp = lane >> 4;
   bf16* Wt = (bf16*)(smem + S::HEAD);
   {
+    // every 16-byte load issued before the first LDS write: one memory
+    // latency, not one per piece
+    constexpr int NP = BwdCfg<Q>::NTILE * 32, WI = (NP + NT - 1) / NT;
     const bf16* src = wsum + m * (int64_t)(BwdCfg<Q>::NTILE * 256);
-    for (int i = threadIdx.x; i < BwdCfg<Q>::NTILE * 32; i += NT)
-      *(bf16x8*)(Wt + i * 8) = *(const bf16x8*)(src + i * 8);
+    bf16x8 wv[WI];
+#pragma unroll
+    for (int it = 0; it < WI; ++it) {
+      const int i = threadIdx.x + it * NT;
+      if (i < NP) wv[it] = *(const bf16x8*)(src + i * 8);
+    }
+#pragma unroll
+    for (int it = 0; it < WI; ++it) {
+      const int i = threadIdx.x + it * NT;
+      if (i < NP) *(bf16x8*)(Wt + i * 8) = wv[it];
+    }
   }
   __syncthreads();
 
