@@ -126,6 +126,30 @@ def test_workload_names():
         bench.workload("nonsense")
 
 
+def test_metric_names():
+    """The headline workload reports the headline metric; any other workload
+    names itself, so its line is never mistaken for the headline's."""
+    head = bench.workload(bench.HEADLINE)
+    assert bench.metric_name(head) == bench.METRIC
+    other = bench.workload("longest_L256k_N512")
+    assert "longest_L256k_N512" in bench.metric_name(other)
+    assert "longest_L256k_N512" in bench.metric_name(other, backward=True)
+    assert "L=64K,N=256" in bench.metric_name(head, backward=True)
+
+
+def test_backward_fast_path_rule():
+    """bench's model of which sizes take the MFMA backward matches the
+    library's rule: bf16, head size 64, state 64/128/256 with chunk 64-256,
+    or state 512 with chunk 256."""
+    cases = [((64, 256, "bf16", 64), True), ((512, 256, "bf16", 64), True),
+             ((512, 128, "bf16", 64), False), ((256, 64, "f32", 64), False),
+             ((256, 256, "bf16", 32), False), ((96, 128, "bf16", 64), False)]
+    for (N, Q, dt, P), fast in cases:
+        w = ssd_inputs.custom(name="m", batch=1, seqlen=512, nheads=2, headdim=P, dstate=N,
+                              ngroups=1, chunk_size=Q, dtype=dt, init_state=False, seed=0)
+        assert bench.backward_fast(w) == fast, (N, Q, dt, P)
+
+
 @pytest.mark.parametrize("extra", [[], ["--backward"]])
 def test_more_than_one_gpu_is_refused(extra):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2", *extra],
